@@ -1,0 +1,150 @@
+"""TEST INFRASTRUCTURE ONLY: ctypes front end of liboracle.so, the plain C
+double-precision oracle (oracle.c). Only the tests, the smoke check and the
+benchmark's CPU-baseline leg import this; the product path never does.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = ctypes.CDLL(os.path.join(HERE, "liboracle.so"))
+_p, _i32 = ctypes.c_void_p, ctypes.c_int32
+
+_lib.oracle_e4m3.argtypes = [ctypes.c_uint8]
+_lib.oracle_e4m3.restype = ctypes.c_double
+_lib.oracle_bf16.argtypes = [ctypes.c_uint16]
+_lib.oracle_bf16.restype = ctypes.c_double
+_lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+_lib.oracle_round_bf16.restype = ctypes.c_uint16
+_lib.oracle_idx_score.argtypes = [_p] * 6 + [_i32] * 3 + [_p, _p]
+_lib.oracle_topk.argtypes = [_p, _p] + [_i32] * 4 + [_p]
+_lib.oracle_sparse_mla.argtypes = [_p, _p, _i32, _p, _p] + [_i32] * 4 + [ctypes.c_double] + [_p] * 3
+_lib.oracle_is_full_layer.argtypes = [_i32, _i32, _p]
+for _f in ("oracle_idx_score", "oracle_topk", "oracle_sparse_mla", "oracle_is_full_layer",
+           "oracle_indexshare"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+SCHED_GROUP4, SCHED_GLM52, SCHED_ALL_FULL, SCHED_MASK = 0, 1, 2, 3
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("q8", "q_scale", "w", "k8", "k_scale", "q", "kv", "kv_scale",
+                                  "out", "lse")]
+
+
+_lib.oracle_indexshare.argtypes = [ctypes.POINTER(_Layer), _i32, _i32, _p, _i32, _i32, _p] + \
+    [_i32] * 4 + [ctypes.c_double, _p]
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError("oracle %s rejected its input (code %d)" % (what, rc))
+
+
+def e4m3(code):
+    return _lib.oracle_e4m3(int(code))
+
+
+def bf16(bits):
+    return _lib.oracle_bf16(int(bits))
+
+
+def round_bf16(x):
+    return int(_lib.oracle_round_bf16(float(x)))
+
+
+def idx_score(q8, q_scale, w, k8, k_scale, vis_len, want64=False):
+    """q8[B,T,32,128] u8, q_scale/w[B,T,32] f32, k8[B,L,128] u8, k_scale[B,L] f32,
+    vis_len[B,T] i32 -> scores[B,T,L] f32 (and the double values if want64)"""
+    q8, k8 = _c(q8, np.uint8), _c(k8, np.uint8)
+    q_scale, w, k_scale = _c(q_scale, np.float32), _c(w, np.float32), _c(k_scale, np.float32)
+    vis_len = _c(vis_len, np.int32)
+    B, T = q8.shape[0], q8.shape[1]
+    L = k8.shape[1]
+    assert q8.shape == (B, T, 32, 128) and k8.shape == (B, L, 128)
+    assert q_scale.shape == (B, T, 32) and w.shape == (B, T, 32) and k_scale.shape == (B, L)
+    assert vis_len.shape == (B, T)
+    out = np.empty((B, T, L), np.float32)
+    out64 = np.empty((B, T, L), np.float64) if want64 else None
+    _check(_lib.oracle_idx_score(q8.ctypes.data, q_scale.ctypes.data, w.ctypes.data,
+                                 k8.ctypes.data, k_scale.ctypes.data, vis_len.ctypes.data, B, T,
+                                 L, out.ctypes.data, out64.ctypes.data if want64 else None),
+           "idx_score")
+    return (out, out64) if want64 else out
+
+
+def topk(scores, vis_len, k):
+    scores = _c(scores, np.float32)
+    vis_len = _c(vis_len, np.int32)
+    B, T, L = scores.shape
+    idx = np.empty((B, T, k), np.int32)
+    _check(_lib.oracle_topk(scores.ctypes.data, vis_len.ctypes.data, B, T, L, k, idx.ctypes.data),
+           "topk")
+    return idx
+
+
+def sparse_mla(q, kv, kv_scale, idx, sm_scale, L=None, want64=False):
+    """q[B,T,64,576] bf16 bits (u16), kv[B,L,576] bf16 bits (u16) or E4M3 codes (u8) with
+    kv_scale[B,L], idx[B,T,k] -> (out bf16 bits [B,T,64,512], lse f32 [B,T,64][, out64])"""
+    q = _c(q, np.uint16)
+    fp8 = kv.dtype == np.uint8
+    kv = _c(kv, np.uint8 if fp8 else np.uint16)
+    idx = _c(idx, np.int32)
+    B, T = q.shape[0], q.shape[1]
+    L = kv.shape[1] if L is None else L
+    k = idx.shape[-1]
+    ks = _c(kv_scale, np.float32) if fp8 else None
+    out = np.empty((B, T, 64, 512), np.uint16)
+    lse = np.empty((B, T, 64), np.float32)
+    out64 = np.empty((B, T, 64, 512), np.float64) if want64 else None
+    _check(_lib.oracle_sparse_mla(q.ctypes.data, kv.ctypes.data, 1 if fp8 else 0,
+                                  ks.ctypes.data if fp8 else None, idx.ctypes.data, B, T, L, k,
+                                  float(sm_scale), out.ctypes.data, lse.ctypes.data,
+                                  out64.ctypes.data if want64 else None), "sparse_mla")
+    return (out, lse, out64) if want64 else (out, lse)
+
+
+def is_full_layer(sched, l, mask=None):
+    buf = None if mask is None else np.ascontiguousarray(mask, np.uint8)
+    return bool(_lib.oracle_is_full_layer(sched, l, buf.ctypes.data if buf is not None else None))
+
+
+def indexshare(layers, sched, vis_len, k, sm_scale, kv_fp8=False, mtp_steps=0, mask=None):
+    """layers: list of dicts of numpy arrays (q8, q_scale, w, k8, k_scale on full layers;
+    q, kv, kv_scale always). Returns (outs, lses, idx_out)."""
+    n = len(layers)
+    keep = []
+    arr = (_Layer * n)()
+    vis_len = _c(vis_len, np.int32)
+    B, T = vis_len.shape
+    L = None
+    outs, lses = [], []
+    for i, ly in enumerate(layers):
+        conv = {}
+        for f, dt in (("q8", np.uint8), ("q_scale", np.float32), ("w", np.float32),
+                      ("k8", np.uint8), ("k_scale", np.float32), ("q", np.uint16),
+                      ("kv", np.uint8 if kv_fp8 else np.uint16), ("kv_scale", np.float32)):
+            if ly.get(f) is not None:
+                conv[f] = _c(ly[f], dt)
+                setattr(arr[i], f, conv[f].ctypes.data)
+        if "kv" in conv:
+            L = conv["kv"].shape[1]
+        o = np.empty((B, T, 64, 512), np.uint16)
+        s = np.empty((B, T, 64), np.float32)
+        arr[i].out, arr[i].lse = o.ctypes.data, s.ctypes.data
+        outs.append(o)
+        lses.append(s)
+        keep.append(conv)
+    n_full = 1 if mtp_steps else sum(is_full_layer(sched, l, mask) for l in range(n))
+    idx_out = np.empty((n_full, B, T, k), np.int32)
+    mbuf = None if mask is None else np.ascontiguousarray(mask, np.uint8)
+    _check(_lib.oracle_indexshare(arr, n, sched, mbuf.ctypes.data if mbuf is not None else None,
+                                  mtp_steps, 1 if kv_fp8 else 0, vis_len.ctypes.data, B, T, L, k,
+                                  float(sm_scale), idx_out.ctypes.data), "indexshare")
+    return outs, lses, idx_out

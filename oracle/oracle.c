@@ -1,0 +1,305 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY: plain CPU oracle of the DSA +
+ * IndexShare attention path (see oracle.h for what is computed and which page
+ * passage each part follows). Single-threaded, double precision, no blocking
+ * or reordering beyond the definitions. Not used by the product path.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define IDX_HEADS 32 /* "32 个 Indexer Heads" (architecture panel) */
+#define IDX_DIM 128  /* indexer key/query width: a reading, not on the pages */
+#define ATT_HEADS 64 /* "Attention 64 Heads" (architecture panel) */
+#define KV_LATENT 512 /* "KV 低秩联合压缩 Rank 512" (kv_lora_rank) */
+#define KV_ROPE 64    /* decoupled rope part of each cached row: a reading */
+#define KV_DIM (KV_LATENT + KV_ROPE)
+
+/* OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits.
+ * exponent field 0: subnormal (m/8) * 2^-6; S.1111.111: NaN; else
+ * (1 + m/8) * 2^(e-7). Largest finite value 448. */
+double oracle_e4m3(uint8_t code) {
+  int s = code >> 7;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9); /* (m/8) * 2^-6 */
+  else
+    v = ldexp(8.0 + (double)m, e - 10); /* (1 + m/8) * 2^(e-7) */
+  return s ? -v : v;
+}
+
+/* bf16 is the top half of an IEEE binary32 */
+double oracle_bf16(uint16_t bits) {
+  union { uint32_t u; float f; } c;
+  c.u = (uint32_t)bits << 16;
+  return (double)c.f;
+}
+
+/* Round a finite double to the nearest bf16 (8 significant bits), ties to
+ * even, directly from the double (no intermediate fp32 rounding). */
+uint16_t oracle_round_bf16(double x) {
+  uint16_t sign = 0;
+  if (signbit(x)) { sign = 0x8000; x = -x; }
+  if (x == 0.0) return sign;
+  if (isinf(x)) return (uint16_t)(sign | 0x7F80);
+  int e;
+  double fr = frexp(x, &e); /* x = fr * 2^e, fr in [0.5, 1) */
+  /* binary32 normal range: exponent of the leading bit e-1 >= -126 */
+  int lead = e - 1;
+  double q;
+  if (lead < -126) {
+    /* subnormal bf16: step 2^-133 */
+    q = rint(ldexp(x, 133));
+    union { uint32_t u; float f; } c;
+    c.f = (float)ldexp(q, -133); /* exact: q < 2^7 times a power of two */
+    return (uint16_t)(sign | (c.u >> 16));
+  }
+  q = rint(ldexp(fr, 8)); /* 8 significant bits: in [128, 256] */
+  double v = ldexp(q, e - 8);
+  if (v > 3.3895313892515355e38) return (uint16_t)(sign | 0x7F80); /* above the largest bf16 */
+  union { uint32_t u; float f; } c;
+  c.f = (float)v; /* exact: v has 8 significant bits and is in range */
+  return (uint16_t)(sign | (c.u >> 16));
+}
+
+static int clamp_vis(int32_t v, int32_t L) {
+  if (v < 0) return 0;
+  if (v > L) return L;
+  return v;
+}
+
+int oracle_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
+                     const uint8_t* k8, const float* k_scale,
+                     const int32_t* vis_len, int32_t B, int32_t T, int32_t L,
+                     float* scores, double* scores64) {
+  if (!q8 || !q_scale || !w || !k8 || !k_scale || !vis_len || !scores) return 1;
+  if (B < 0 || T < 0 || L < 0) return 2;
+  double qd[IDX_HEADS][IDX_DIM];
+  double wq[IDX_HEADS];
+  double kd[IDX_DIM];
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t t = 0; t < T; ++t) {
+      const size_t bt = (size_t)b * T + t;
+      for (int j = 0; j < IDX_HEADS; ++j) {
+        for (int i = 0; i < IDX_DIM; ++i) {
+          qd[j][i] = oracle_e4m3(q8[(bt * IDX_HEADS + j) * IDX_DIM + i]);
+          if (isnan(qd[j][i])) return 3;
+        }
+        /* the head weight and the query's dequantisation scale are both
+         * positive per-head factors; their product is exact in double */
+        wq[j] = (double)w[bt * IDX_HEADS + j] * (double)q_scale[bt * IDX_HEADS + j];
+      }
+      const int vis = clamp_vis(vis_len[bt], L);
+      float* srow = scores + bt * (size_t)L;
+      double* s64 = scores64 ? scores64 + bt * (size_t)L : NULL;
+      for (int32_t s = 0; s < L; ++s) {
+        if (s >= vis) {
+          srow[s] = -INFINITY;
+          if (s64) s64[s] = -INFINITY;
+          continue;
+        }
+        for (int i = 0; i < IDX_DIM; ++i) {
+          kd[i] = oracle_e4m3(k8[((size_t)b * L + s) * IDX_DIM + i]);
+          if (isnan(kd[i])) return 3;
+        }
+        double sum = 0.0;
+        for (int j = 0; j < IDX_HEADS; ++j) {
+          double d = 0.0; /* exact: see the exactness pin in the tests */
+          for (int i = 0; i < IDX_DIM; ++i) d += qd[j][i] * kd[i];
+          double r = d > 0.0 ? d : 0.0; /* ReLU */
+          sum += wq[j] * r;
+        }
+        double I = (double)k_scale[(size_t)b * L + s] * sum;
+        srow[s] = (float)I;
+        if (s64) s64[s] = I;
+      }
+    }
+  }
+  return 0;
+}
+
+typedef struct {
+  float score;
+  int32_t pos;
+} scored_pos;
+
+/* strict total order: higher score first, then lower position */
+static int cmp_rank(const void* a, const void* b) {
+  const scored_pos* x = (const scored_pos*)a;
+  const scored_pos* y = (const scored_pos*)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+static int cmp_int(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+int oracle_topk(const float* scores, const int32_t* vis_len, int32_t B,
+                int32_t T, int32_t L, int32_t k, int32_t* idx) {
+  if (!scores || !vis_len || !idx) return 1;
+  if (B < 0 || T < 0 || L < 0 || k <= 0) return 2;
+  scored_pos* buf = (scored_pos*)malloc(sizeof(scored_pos) * (size_t)(L > 0 ? L : 1));
+  int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  if (!buf || !sel) { free(buf); free(sel); return 4; }
+  for (size_t bt = 0; bt < (size_t)B * T; ++bt) {
+    const int vis = clamp_vis(vis_len[bt], L);
+    const float* srow = scores + bt * (size_t)L;
+    for (int s = 0; s < vis; ++s) {
+      if (isnan(srow[s])) { free(buf); free(sel); return 3; }
+      buf[s].score = srow[s];
+      buf[s].pos = s;
+    }
+    qsort(buf, (size_t)vis, sizeof(scored_pos), cmp_rank);
+    const int m = vis < k ? vis : k;
+    for (int i = 0; i < m; ++i) sel[i] = buf[i].pos;
+    qsort(sel, (size_t)m, sizeof(int32_t), cmp_int);
+    int32_t* out = idx + bt * (size_t)k;
+    for (int i = 0; i < k; ++i) out[i] = i < m ? sel[i] : -1;
+  }
+  free(buf);
+  free(sel);
+  return 0;
+}
+
+int oracle_sparse_mla(const uint16_t* q, const void* kv, int32_t kv_fp8,
+                      const float* kv_scale, const int32_t* idx, int32_t B,
+                      int32_t T, int32_t L, int32_t k, double sm_scale,
+                      uint16_t* out, float* lse, double* out64) {
+  if (!q || !kv || !idx || !out || !lse) return 1;
+  if (kv_fp8 && !kv_scale) return 1;
+  if (B < 0 || T < 0 || L < 0 || k <= 0) return 2;
+  double* rows = (double*)malloc(sizeof(double) * (size_t)k * KV_DIM);
+  double* z = (double*)malloc(sizeof(double) * (size_t)k);
+  if (!rows || !z) { free(rows); free(z); return 4; }
+  const uint16_t* kv16 = (const uint16_t*)kv;
+  const uint8_t* kv8 = (const uint8_t*)kv;
+  int rc = 0;
+  for (int32_t b = 0; b < B && !rc; ++b) {
+    for (int32_t t = 0; t < T && !rc; ++t) {
+      const size_t bt = (size_t)b * T + t;
+      const int32_t* sel = idx + bt * (size_t)k;
+      /* gather the selected rows, decoded exactly */
+      int n = 0;
+      for (int i = 0; i < k; ++i) {
+        const int32_t s = sel[i];
+        if (s == -1) continue;
+        if (s < 0 || s >= L) { rc = 2; break; }
+        const size_t base = ((size_t)b * L + s) * KV_DIM;
+        for (int d = 0; d < KV_DIM; ++d) {
+          double v;
+          if (kv_fp8) {
+            v = oracle_e4m3(kv8[base + d]);
+            if (isnan(v)) { rc = 3; break; }
+            v *= (double)kv_scale[(size_t)b * L + s]; /* exact */
+          } else {
+            v = oracle_bf16(kv16[base + d]);
+          }
+          rows[(size_t)n * KV_DIM + d] = v;
+        }
+        ++n;
+      }
+      if (rc) break;
+      for (int h = 0; h < ATT_HEADS; ++h) {
+        const uint16_t* qh = q + (bt * ATT_HEADS + h) * KV_DIM;
+        uint16_t* oh = out + (bt * ATT_HEADS + h) * KV_LATENT;
+        double* o64 = out64 ? out64 + (bt * ATT_HEADS + h) * KV_LATENT : NULL;
+        if (n == 0) {
+          for (int v = 0; v < KV_LATENT; ++v) {
+            oh[v] = 0;
+            if (o64) o64[v] = 0.0;
+          }
+          lse[bt * ATT_HEADS + h] = -INFINITY;
+          continue;
+        }
+        double mu = -INFINITY;
+        for (int i = 0; i < n; ++i) {
+          double dot = 0.0;
+          for (int d = 0; d < KV_DIM; ++d) dot += oracle_bf16(qh[d]) * rows[(size_t)i * KV_DIM + d];
+          z[i] = sm_scale * dot;
+          if (z[i] > mu) mu = z[i];
+        }
+        double denom = 0.0;
+        for (int i = 0; i < n; ++i) {
+          z[i] = exp(z[i] - mu); /* z now holds e_i */
+          denom += z[i];
+        }
+        for (int v = 0; v < KV_LATENT; ++v) {
+          double acc = 0.0;
+          for (int i = 0; i < n; ++i) acc += z[i] * rows[(size_t)i * KV_DIM + v];
+          const double o = acc / denom;
+          oh[v] = oracle_round_bf16(o);
+          if (o64) o64[v] = o;
+        }
+        lse[bt * ATT_HEADS + h] = (float)(mu + log(denom));
+      }
+    }
+  }
+  free(rows);
+  free(z);
+  return rc;
+}
+
+/* "IndexShare：四层共用一次搜索结果": layers 0 and 1 have their own indexer;
+ * from layer 2 on every fourth layer (2, 6, 10, ..., 74) has one and passes
+ * its Top-k to the three layers after it. GROUP4 is the plain "first layer of
+ * every four" wording of the engineering-report wiki. */
+int oracle_is_full_layer(int32_t sched, int32_t l, const uint8_t* mask) {
+  if (l < 0) return 0;
+  switch (sched) {
+    case ORACLE_SCHED_GROUP4:
+      return l % 4 == 0;
+    case ORACLE_SCHED_GLM52:
+      if (l == 0 || l == 1) return 1;
+      return (l - 2) % 4 == 0;
+    case ORACLE_SCHED_ALL_FULL:
+      return 1;
+    case ORACLE_SCHED_MASK:
+      return mask ? mask[l] != 0 : 0;
+    default:
+      return 0;
+  }
+}
+
+int oracle_indexshare(const oracle_layer* layers, int32_t n_layers,
+                      int32_t sched, const uint8_t* mask, int32_t mtp_steps,
+                      int32_t kv_fp8, const int32_t* vis_len, int32_t B,
+                      int32_t T, int32_t L, int32_t k, double sm_scale,
+                      int32_t* idx_out) {
+  if (!layers || !vis_len || !idx_out || n_layers <= 0) return 1;
+  if (mtp_steps < 0 || (mtp_steps > 0 && mtp_steps != n_layers)) return 2;
+  const size_t per = (size_t)B * T * k;
+  float* scores = (float*)malloc(sizeof(float) * (size_t)B * T * (size_t)(L > 0 ? L : 1));
+  if (!scores) return 4;
+  const int32_t* cur = NULL;
+  int32_t nfull = 0;
+  int rc = 0;
+  for (int32_t l = 0; l < n_layers && !rc; ++l) {
+    const oracle_layer* ly = &layers[l];
+    const int full = mtp_steps > 0 ? (l == 0) : oracle_is_full_layer(sched, l, mask);
+    if (full) {
+      int32_t* dst = idx_out + (size_t)nfull * per;
+      rc = oracle_idx_score(ly->q8, ly->q_scale, ly->w, ly->k8, ly->k_scale, vis_len, B, T, L,
+                            scores, NULL);
+      if (!rc) rc = oracle_topk(scores, vis_len, B, T, L, k, dst);
+      cur = dst;
+      ++nfull;
+    } else if (!cur) {
+      rc = 2; /* a shared layer with no earlier full layer */
+    }
+    if (rc) break;
+    /* KV Share: every draft step reads the first step's cache */
+    const oracle_layer* kvl = mtp_steps > 0 ? &layers[0] : ly;
+    rc = oracle_sparse_mla(ly->q, kvl->kv, kv_fp8, kvl->kv_scale, cur, B, T, L, k, sm_scale,
+                           ly->out, ly->lse, NULL);
+  }
+  free(scores);
+  return rc;
+}

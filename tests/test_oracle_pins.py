@@ -1,0 +1,392 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: published
+format values, library routines (torch's float8/bf16 casts, torch softmax),
+exact integer arithmetic, brute force on tiny inputs, closed forms and the
+page's layer list.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+def _finite_codes(n, rs=rng):
+    c = rs.integers(0, 256, size=n).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x3C  # avoid the NaN codes
+    return c
+
+
+# ------------------------------------------------------------------ E4M3 / bf16
+def test_e4m3_matches_torch_float8_all_codes():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        v = oracle.e4m3(c)
+        if np.isnan(ref[c]):
+            assert np.isnan(v), c
+        else:
+            assert v == ref[c] and np.signbit(v) == np.signbit(ref[c]), (c, v, ref[c])
+
+
+def test_e4m3_ocp_spot_values():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "e4m3_ocp_spot.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        code, val = line.split()
+        v = oracle.e4m3(int(code, 16))
+        if val == "nan":
+            assert np.isnan(v)
+        else:
+            assert v == float(val) and np.signbit(v) == val.startswith("-"), (code, v)
+        n += 1
+    assert n == 12
+
+
+def test_bf16_decode_matches_torch():
+    bits = rng.integers(0, 1 << 16, size=4000).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # finite only
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16(int(b)) for b in bits])
+    assert np.array_equal(got, ref)
+
+
+def test_round_bf16_against_torch_and_ties():
+    # values exactly representable in fp32: torch's fp32 -> bf16 cast is RNE
+    x = (rng.standard_normal(3000) * 10.0 ** rng.integers(-5, 5, size=3000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.round_bf16(float(v)) for v in x], np.uint16)
+    assert np.array_equal(got, ref)
+    # exact ties go to the even significand
+    assert oracle.round_bf16(1.0 + 2.0 ** -8) == 0x3F80  # tie between 1 and 1+2^-7 -> 1
+    assert oracle.round_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82  # tie -> 1+2^-6 (even)
+    assert oracle.round_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -30)) == 0xBF81  # just above a tie
+
+
+# ------------------------------------------------------------------ indexer
+def _idx_inputs(B, T, L, rs):
+    q8 = _finite_codes(B * T * 32 * 128, rs).reshape(B, T, 32, 128)
+    k8 = _finite_codes(B * L * 128, rs).reshape(B, L, 128)
+    qs = rs.uniform(0.001, 0.1, size=(B, T, 32)).astype(np.float32)
+    w = rs.uniform(0, 1, size=(B, T, 32)).astype(np.float32)
+    ks = rs.uniform(0.001, 0.1, size=(B, L)).astype(np.float32)
+    return q8, qs, w, k8, ks
+
+
+def _dec(codes):
+    lut = np.array([oracle.e4m3(c) for c in range(256)])
+    return lut[codes]
+
+
+def test_idx_score_brute_force_numpy():
+    rs = np.random.default_rng(7)
+    B, T, L = 2, 3, 37
+    q8, qs, w, k8, ks = _idx_inputs(B, T, L, rs)
+    vis = np.array([[37, 20, 0], [1, 37, 50]], np.int32)
+    got, got64 = oracle.idx_score(q8, qs, w, k8, ks, vis, want64=True)
+    d = np.einsum("btjd,bsd->btjs", _dec(q8), _dec(k8))  # library contraction, float64
+    ref = ks[:, None, :] * np.einsum("btj,btjs->bts", w.astype(np.float64) * qs, np.maximum(d, 0))
+    for b in range(B):
+        for t in range(T):
+            v = min(max(vis[b, t], 0), L)
+            assert np.all(np.isneginf(got[b, t, v:])) and np.all(np.isneginf(got64[b, t, v:]))
+            np.testing.assert_allclose(got64[b, t, :v], ref[b, t, :v], rtol=1e-13, atol=0)
+            np.testing.assert_array_equal(got[b, t, :v], got64[b, t, :v].astype(np.float32))
+
+
+def test_idx_score_dot_is_exact():
+    # one head, w = scales = 1: the double score equals relu(q.k) exactly; every E4M3
+    # value is an integer multiple of 2^-9, so q.k * 2^18 is an exact integer
+    rs = np.random.default_rng(8)
+    L = 64
+    q8, qs, w, k8, ks = _idx_inputs(1, 1, L, rs)
+    w[:] = 0
+    w[0, 0, 5] = 1
+    qs[:] = 1
+    ks[:] = 1
+    _, got64 = oracle.idx_score(q8, qs, w, k8, ks, np.array([[L]], np.int32), want64=True)
+    qi = [int(Fraction(oracle.e4m3(c)) * 512) for c in q8[0, 0, 5]]
+    for s in range(L):
+        ki = [int(Fraction(oracle.e4m3(c)) * 512) for c in k8[0, s]]
+        exact = Fraction(sum(a * b for a, b in zip(qi, ki)), 1 << 18)
+        assert Fraction(got64[0, 0, s]) == max(exact, Fraction(0)), s
+
+
+def test_idx_score_closed_forms():
+    L = 8
+    q8 = np.full((1, 1, 32, 128), 0x44, np.uint8)  # 3.0
+    k8 = np.full((1, L, 128), 0x30, np.uint8)  # 0.5
+    k8[0, 3] = 0xB0  # -0.5 -> every head negative -> 0
+    qs = np.linspace(0.5, 2.0, 32, dtype=np.float32).reshape(1, 1, 32)
+    w = np.linspace(0.0, 1.0, 32, dtype=np.float32).reshape(1, 1, 32)
+    ks = np.arange(1, L + 1, dtype=np.float32).reshape(1, L) * 0.25
+    vis = np.array([[L]], np.int32)
+    _, s64 = oracle.idx_score(q8, qs, w, k8, ks, vis, want64=True)
+    d = 128 * 3.0 * 0.5
+    for s in range(L):
+        exp = 0.0 if s == 3 else float(ks[0, s]) * sum(float(w[0, 0, j]) * float(qs[0, 0, j]) * d
+                                                      for j in range(32))
+        assert s64[0, 0, s] == pytest.approx(exp, rel=1e-15, abs=0)
+    # doubling every head weight doubles every score exactly
+    s1 = oracle.idx_score(q8, qs, w, k8, ks, vis)
+    s2 = oracle.idx_score(q8, qs, 2 * w, k8, ks, vis)
+    np.testing.assert_array_equal(s2, 2 * s1)
+
+
+def test_idx_score_query_opposite_key_is_zero():
+    rs = np.random.default_rng(9)
+    q8, qs, w, k8, ks = _idx_inputs(1, 1, 4, rs)
+    q8[0, 0, :, :] = k8[0, 2, :] ^ 0x80  # every head = -key 2
+    s = oracle.idx_score(q8, qs, w, k8, ks, np.array([[4]], np.int32))
+    assert s[0, 0, 2] == 0.0 and not np.signbit(s[0, 0, 2])
+
+
+def test_idx_score_vis_len_clamped():
+    rs = np.random.default_rng(10)
+    q8, qs, w, k8, ks = _idx_inputs(1, 2, 5, rs)
+    s = oracle.idx_score(q8, qs, w, k8, ks, np.array([[-3, 99]], np.int32))
+    assert np.all(np.isneginf(s[0, 0])) and np.all(np.isfinite(s[0, 1]))
+
+
+# ------------------------------------------------------------------ top-k
+def _brute_topk(scores, vis, k):
+    order = sorted(range(vis), key=lambda s: (-float(scores[s]), s))
+    sel = sorted(order[:k])
+    return sel + [-1] * (k - len(sel))
+
+
+@pytest.mark.parametrize("L,k", [(1, 1), (7, 4), (2047, 2048), (2048, 2048), (2049, 2048),
+                                 (4096, 2048), (4096, 64), (300, 100)])
+def test_topk_brute_force_with_ties(L, k):
+    rs = np.random.default_rng(L * 31 + k)
+    s = rs.integers(0, 50, size=(2, 2, L)).astype(np.float32) * 0.25  # many ties
+    vis = np.array([[L, max(L // 2, 1)], [max(L - 1, 0), 0]], np.int32)
+    got = oracle.topk(s, vis, k)
+    for b in range(2):
+        for t in range(2):
+            assert list(got[b, t]) == _brute_topk(s[b, t], vis[b, t], k), (b, t)
+
+
+def test_topk_properties():
+    rs = np.random.default_rng(11)
+    L, k = 5000, 2048
+    s = rs.standard_normal((1, 1, L)).astype(np.float32)
+    idx = oracle.topk(s, np.array([[L]], np.int32), k)[0, 0]
+    assert len(set(idx)) == k and np.all(np.diff(idx) > 0)
+    sel = np.zeros(L, bool)
+    sel[idx] = True
+    assert s[0, 0, sel].min() >= s[0, 0, ~sel].max()
+    # scaling by a power of two changes nothing
+    idx2 = oracle.topk(s * 8, np.array([[L]], np.int32), k)[0, 0]
+    assert np.array_equal(idx, idx2)
+    # all equal -> the first k positions
+    eq = np.ones((1, 1, L), np.float32)
+    assert np.array_equal(oracle.topk(eq, np.array([[L]], np.int32), k)[0, 0], np.arange(k))
+    # fewer visible than k -> all of them then -1
+    got = oracle.topk(s, np.array([[100]], np.int32), k)[0, 0]
+    assert np.array_equal(got[:100], np.arange(100)) and np.all(got[100:] == -1)
+
+
+def test_topk_signed_zero_is_a_tie_and_nan_rejected():
+    s = np.array([[[-0.0, 0.0, -0.0, 1.0]]], np.float32)
+    assert list(oracle.topk(s, np.array([[4]], np.int32), 2)[0, 0]) == [0, 3]
+    s[0, 0, 1] = np.nan
+    with pytest.raises(ValueError):
+        oracle.topk(s, np.array([[4]], np.int32), 2)
+
+
+# ------------------------------------------------------------------ attention
+def _bf16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def _bits_to_f64(b):
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def _dense_ref(q, rows, sm):
+    """dense softmax attention with torch (float64): q[64,576], rows[n,576]"""
+    qt = torch.from_numpy(q)
+    rt = torch.from_numpy(rows)
+    z = sm * (qt @ rt.T)
+    p = torch.softmax(z, dim=-1)
+    return (p @ rt[:, :512]).numpy(), torch.logsumexp(z, dim=-1).numpy()
+
+
+def test_sparse_mla_k_equals_L_matches_dense_softmax():
+    rs = np.random.default_rng(12)
+    B, T, L = 2, 2, 96
+    q = _bf16_bits(rs.standard_normal((B, T, 64, 576)))
+    kv = _bf16_bits(rs.standard_normal((B, L, 576)))
+    idx = np.broadcast_to(np.arange(L, dtype=np.int32), (B, T, L)).copy()
+    out, lse, out64 = oracle.sparse_mla(q, kv, None, idx, 1 / 24, want64=True)
+    for b in range(B):
+        for t in range(T):
+            ref, rl = _dense_ref(_bits_to_f64(q[b, t]), _bits_to_f64(kv[b]), 1 / 24)
+            np.testing.assert_allclose(out64[b, t], ref, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(lse[b, t], rl, rtol=1e-6)
+            # output rounding is RNE of the double result
+            assert all(oracle.round_bf16(v) == o for v, o in
+                       zip(out64[b, t].ravel()[:300], out[b, t].ravel()[:300]))
+
+
+def test_sparse_mla_fp8_rows_match_dense_on_dequantised_values():
+    rs = np.random.default_rng(13)
+    L = 40
+    q = _bf16_bits(rs.standard_normal((1, 1, 64, 576)))
+    codes = _finite_codes(L * 576, rs).reshape(1, L, 576)
+    sc = rs.uniform(0.001, 0.02, size=(1, L)).astype(np.float32)
+    idx = np.arange(L, dtype=np.int32).reshape(1, 1, L)[:, :, ::-1].copy()
+    out, lse, out64 = oracle.sparse_mla(q, codes, sc, idx, 1 / 24, want64=True)
+    rows = _dec(codes[0]) * sc[0][:, None].astype(np.float64)
+    ref, rl = _dense_ref(_bits_to_f64(q[0, 0]), rows, 1 / 24)
+    np.testing.assert_allclose(out64[0, 0], ref, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], rl, rtol=1e-6)
+
+
+def test_sparse_mla_special_cases():
+    rs = np.random.default_rng(14)
+    L, k = 50, 8
+    q = _bf16_bits(rs.standard_normal((1, 1, 64, 576)))
+    kv = _bf16_bits(rs.standard_normal((1, L, 576)))
+    # one valid index: out = the row's latent part, lse = its logit
+    idx = np.full((1, 1, k), -1, np.int32)
+    idx[0, 0, 3] = 17
+    out, lse = oracle.sparse_mla(q, kv, None, idx, 1 / 24)
+    for h in range(64):
+        assert np.array_equal(out[0, 0, h], kv[0, 17, :512])
+        z = np.dot(_bits_to_f64(q[0, 0, h]), _bits_to_f64(kv[0, 17])) / 24
+        assert lse[0, 0, h] == pytest.approx(z, rel=1e-6, abs=1e-6)
+    # no valid index: zeros and -inf
+    idx[:] = -1
+    out, lse = oracle.sparse_mla(q, kv, None, idx, 1 / 24)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    # q = 0: every selected row has weight 1/n -> the mean
+    sel = np.array([1, 5, 9, 44, 2, 30, 31, 7], np.int32)
+    zero_q = np.zeros_like(q)
+    _, _, o64 = oracle.sparse_mla(zero_q, kv, None, sel.reshape(1, 1, k), 1 / 24, want64=True)
+    mean = _bits_to_f64(kv[0, sel, :512]).mean(axis=0)
+    np.testing.assert_allclose(o64[0, 0, 0], mean, rtol=1e-13, atol=1e-15)
+    # permuting idx changes nothing (up to double rounding)
+    _, _, a64 = oracle.sparse_mla(q, kv, None, sel.reshape(1, 1, k), 1 / 24, want64=True)
+    _, _, b64 = oracle.sparse_mla(q, kv, None, sel[::-1].copy().reshape(1, 1, k), 1 / 24,
+                                  want64=True)
+    np.testing.assert_allclose(a64, b64, rtol=1e-12, atol=1e-15)
+    # out-of-range positions are rejected
+    with pytest.raises(ValueError):
+        oracle.sparse_mla(q, kv, None, np.full((1, 1, k), L, np.int32), 1 / 24)
+
+
+def test_sparse_mla_planted_peak_dominates():
+    rs = np.random.default_rng(15)
+    L = 64
+    kvf = rs.standard_normal((1, L, 576))
+    qf = rs.standard_normal((1, 1, 64, 576)) * 0.05
+    # row 10 aligned with every head's query: logit about 20 above the rest
+    kvf[0, 10] = qf[0, 0, 0] / np.linalg.norm(qf[0, 0, 0]) * (20 * 24 / np.linalg.norm(qf[0, 0, 0]))
+    q, kv = _bf16_bits(qf), _bf16_bits(kvf)
+    qf64 = _bits_to_f64(q)
+    for h in range(64):
+        qf64[0, 0, h] = qf64[0, 0, 0]
+    q = _bf16_bits(qf64)
+    idx = np.arange(L, dtype=np.int32).reshape(1, 1, L)
+    _, _, o64 = oracle.sparse_mla(q, kv, None, idx, 1 / 24, want64=True)
+    np.testing.assert_allclose(o64[0, 0, 0], _bits_to_f64(kv[0, 10, :512]), atol=2e-6 * 500)
+
+
+# ------------------------------------------------------------------ IndexShare / MTP
+def _golden_schedule():
+    d = {}
+    for line in open(os.path.join(GOLDEN, "indexshare_schedule.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            key, val = line.split(":")
+            d[key.strip()] = val.split()
+    return d
+
+
+def test_glm52_schedule_equals_page_list():
+    g = _golden_schedule()
+    n = int(g["n_layers"][0])
+    full = [l for l in range(n) if oracle.is_full_layer(oracle.SCHED_GLM52, l)]
+    assert full == [int(x) for x in g["full_layers"]]
+    assert len(full) == int(g["n_full"][0]) and n - len(full) == int(g["n_shared"][0])
+    assert round(100 * (n - len(full)) / n, 1) == float(g["shared_fraction_percent"][0])
+    # one computing layer and three reusing layers per group of four
+    assert [l for l in range(8) if oracle.is_full_layer(oracle.SCHED_GROUP4, l)] == [0, 4]
+    assert all(oracle.is_full_layer(oracle.SCHED_ALL_FULL, l) for l in range(78))
+
+
+def _small_layers(n, B, T, L, rs, kv_fp8=False, same_indexer=False):
+    q8, qs, w, k8, ks = _idx_inputs(B, T, L, rs)
+    layers = []
+    for l in range(n):
+        if not same_indexer:
+            q8, qs, w, k8, ks = _idx_inputs(B, T, L, rs)
+        ly = {"q8": q8, "q_scale": qs, "w": w, "k8": k8, "k_scale": ks,
+              "q": _bf16_bits(rs.standard_normal((B, T, 64, 576)))}
+        if kv_fp8:
+            ly["kv"] = _finite_codes(B * L * 576, rs).reshape(B, L, 576)
+            ly["kv_scale"] = rs.uniform(0.001, 0.01, size=(B, L)).astype(np.float32)
+        else:
+            ly["kv"] = _bf16_bits(rs.standard_normal((B, L, 576)))
+        layers.append(ly)
+    return layers
+
+
+def test_indexshare_shared_layers_use_full_layer_selection():
+    rs = np.random.default_rng(16)
+    B, T, L, k = 1, 2, 300, 64
+    layers = _small_layers(8, B, T, L, rs)
+    vis = np.array([[300, 150]], np.int32)
+    outs, lses, idx_out = oracle.indexshare(layers, oracle.SCHED_GROUP4, vis, k, 1 / 24)
+    assert idx_out.shape[0] == 2
+    for l in range(8):
+        f = l // 4
+        sc = oracle.idx_score(layers[4 * f]["q8"], layers[4 * f]["q_scale"], layers[4 * f]["w"],
+                              layers[4 * f]["k8"], layers[4 * f]["k_scale"], vis)
+        assert np.array_equal(idx_out[f], oracle.topk(sc, vis, k))
+        o, s = oracle.sparse_mla(layers[l]["q"], layers[l]["kv"], None, idx_out[f], 1 / 24)
+        assert np.array_equal(o, outs[l]) and np.array_equal(s, lses[l])
+    # shared layers never read their own indexer inputs
+    for l in (1, 2, 3, 5, 6, 7):
+        for f in ("q8", "q_scale", "w", "k8", "k_scale"):
+            layers[l][f] = None
+    outs2, _, idx2 = oracle.indexshare(layers, oracle.SCHED_GROUP4, vis, k, 1 / 24)
+    assert np.array_equal(idx2, idx_out) and all(np.array_equal(a, b) for a, b in zip(outs, outs2))
+
+
+def test_indexshare_all_full_with_shared_inputs_gives_identical_selections():
+    rs = np.random.default_rng(17)
+    layers = _small_layers(4, 1, 1, 200, rs, same_indexer=True)
+    vis = np.array([[200]], np.int32)
+    _, _, idx_out = oracle.indexshare(layers, oracle.SCHED_ALL_FULL, vis, 32, 1 / 24)
+    assert idx_out.shape[0] == 4 and all(np.array_equal(idx_out[0], idx_out[i]) for i in range(4))
+
+
+def test_mtp_steps_reuse_step0_selection_and_kv():
+    rs = np.random.default_rng(18)
+    B, T, L, k = 2, 1, 256, 64
+    layers = _small_layers(7, B, T, L, rs, kv_fp8=True)
+    vis = np.full((B, T), L, np.int32)
+    outs, lses, idx_out = oracle.indexshare(layers, 0, vis, k, 1 / 24, kv_fp8=True, mtp_steps=7)
+    assert idx_out.shape[0] == 1
+    for s in range(7):
+        o, ls = oracle.sparse_mla(layers[s]["q"], layers[0]["kv"], layers[0]["kv_scale"],
+                                  idx_out[0], 1 / 24)
+        assert np.array_equal(o, outs[s]) and np.array_equal(ls, lses[s])
+    # the same q at every step gives bit-identical outputs
+    for s in range(7):
+        layers[s]["q"] = layers[0]["q"]
+    outs, _, _ = oracle.indexshare(layers, 0, vis, k, 1 / 24, kv_fp8=True, mtp_steps=7)
+    assert all(np.array_equal(outs[0], outs[s]) for s in range(7))
