@@ -1,0 +1,181 @@
+/*
+ * lcs.h -- C ABI of the MI355X (gfx950) DSA + IndexShare attention path.
+ *
+ * Three stages, as the GLM-5.2 pages describe the attention of one layer
+ * ("一枚 Token，怎样穿过 78 层", panel "MLA 压缩，DSA 精读", ailearn GLM-5.2
+ * special edition; and "IndexShare：省掉3/4的索引计算", Hygon DCU forum post):
+ * a light indexer scores every cached position for each query, a Top-2,048
+ * selection keeps the best positions, and core attention reads only those
+ * latent-KV rows. IndexShare ("IndexShare：四层共用一次搜索结果", same special
+ * edition) runs the indexer on some layers and lets the following layers reuse
+ * the selection; the MTP draft steps reuse it too ("MTP：同一位速记员，多猜几枚
+ * 未来 Token": IndexShare and KV Share).
+ *
+ * Fixed shapes: 32 indexer heads x 128 dims (the pages give the 32 heads;
+ * 128 is a reading), 64 attention heads ("Attention 64 Heads"), latent KV rows
+ * of 512 latent dims ("KV 低秩联合压缩 Rank 512") plus 64 rope dims (a reading
+ * of the absorbed MLA form), so 576 dims per cached row.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller, contiguous,
+ *    row-major in the order given, and 16-byte aligned. bf16 values are passed
+ *    as uint16_t bit patterns. FP8 values are OCP E4M3 codes (bias 7, max 448).
+ *  - Calls are asynchronous on `stream` (NULL = the default stream). The
+ *    library never allocates, frees or synchronises, and keeps no state
+ *    between calls except inside caller-provided workspaces.
+ *  - Arguments are validated on the host before any launch. On failure the
+ *    call returns a nonzero lcs_status, launches nothing, and lcs_last_error()
+ *    gives a thread-local description. Launch failures return LCS_ERR_HIP.
+ *    Device faults surface at the caller's next synchronisation.
+ *  - vis_len values are read on the device and clamped to [0, L].
+ *  - Workspaces are scratch device memory of at least the queried size, with
+ *    any content: each call initialises what it uses. One allocation serves
+ *    any number of calls and shapes up to its size. Calls that share a
+ *    workspace must not overlap in time (use one stream, or one workspace per
+ *    stream).
+ */
+#ifndef LCS_H
+#define LCS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  LCS_OK = 0,
+  LCS_ERR_NULL = 1,        /* a required pointer is NULL */
+  LCS_ERR_SHAPE = 2,       /* a size is out of range, or a pointer misaligned */
+  LCS_ERR_UNSUPPORTED = 3, /* k outside [1, 2048], an unknown enum value */
+  LCS_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+  LCS_ERR_HIP = 5          /* a HIP launch or runtime call failed */
+} lcs_status;
+
+typedef enum { LCS_KV_BF16 = 0, LCS_KV_FP8_E4M3 = 1 } lcs_kv_dtype;
+
+#define LCS_IDX_HEADS 32
+#define LCS_IDX_DIM 128
+#define LCS_ATT_HEADS 64
+#define LCS_KV_LATENT 512
+#define LCS_KV_ROPE 64
+#define LCS_KV_DIM 576
+#define LCS_MAX_TOPK 2048
+
+/* Indexer scores ("Indexer 先扫历史": every cached position is scored).
+ * q8      [B][T][32][128] E4M3 query codes
+ * q_scale [B][T][32]      fp32 dequantisation scale per (query, head), > 0
+ * w       [B][T][32]      fp32 head weights
+ * k8      [B][L][128]     E4M3 key codes;  k_scale [B][L] fp32 per-key scale
+ * vis_len [B][T]          int32 visible prefix length of each query
+ * scores  [B][T][L]       fp32 output:
+ *   scores[b,t,s] = k_scale[s] * sum_j w[j]*q_scale[j] * relu(q8[j] . k8[s])
+ *   for s < vis_len[b,t], -inf otherwise.
+ * T <= 4 uses a key-streaming kernel (one pass over the keys, the 32 heads
+ * as the FP8 MFMA M dimension); larger T uses a tiled FP8 MFMA kernel. */
+lcs_status lcs_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
+                         const uint8_t* k8, const float* k_scale,
+                         const int32_t* vis_len, int32_t B, int32_t T, int32_t L,
+                         float* scores, hipStream_t stream);
+
+/* Workspace bytes needed by lcs_topk_select for these sizes. */
+size_t lcs_topk_workspace_bytes(int32_t B, int32_t T, int32_t L, int32_t k);
+
+/* Top-k selection ("核心 Attention 只精看 Top-2,048").
+ * scores [B][T][L] fp32 (no NaN), vis_len [B][T] -> idx [B][T][k] int32:
+ * the min(k, vis_len) positions s < vis_len with the largest scores, equal
+ * scores broken by the lower position, listed in ascending position order and
+ * padded with -1. k in [1, 2048]. Exact (radix select on the fp32 bit
+ * patterns; -0.0 counts as +0.0). */
+lcs_status lcs_topk_select(const float* scores, const int32_t* vis_len, int32_t B,
+                           int32_t T, int32_t L, int32_t k, int32_t* idx,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Workspace bytes needed by lcs_sparse_mla_attn for these sizes. */
+size_t lcs_attn_workspace_bytes(int32_t B, int32_t T, int32_t k);
+
+/* Sparse MLA attention over the selected rows, absorbed form.
+ * q   [B][T][64][576] bf16
+ * kv  [B][L][576] bf16 (LCS_KV_BF16), or E4M3 codes with kv_scale [B][L]
+ *     fp32 (LCS_KV_FP8_E4M3; kv_scale must be NULL for bf16)
+ * idx [B][T][k] int32 positions in [0, L), or -1 for an empty slot
+ * out [B][T][64][512] bf16 = softmax_i(sm_scale * q . kv[idx_i]) . kv[idx_i][0:512]
+ * lse [B][T][64] fp32 natural-log sum of exp of the scaled logits (nullable);
+ * a query with no valid index gets out = 0 and lse = -inf.
+ * Positions outside [-1, L) are a caller error (not checked on the device). */
+lcs_status lcs_sparse_mla_attn(const uint16_t* q, const void* kv,
+                               lcs_kv_dtype kv_dtype, const float* kv_scale,
+                               const int32_t* idx, int32_t B, int32_t T, int32_t L,
+                               int32_t k, float sm_scale, uint16_t* out, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* One layer of the composite call. The indexer fields are read only on
+ * layers that run their own indexer; q/kv/out are used on every layer. */
+typedef struct {
+  const uint8_t* q8;
+  const float* q_scale;
+  const float* w;
+  const uint8_t* k8;
+  const float* k_scale;
+  const uint16_t* q;
+  const void* kv;
+  const float* kv_scale;
+  uint16_t* out;
+  float* lse;
+} lcs_layer;
+
+/* Which layers run their own indexer ("IndexShare：四层共用一次搜索结果").
+ *  GROUP4   : layer l is full iff l % 4 == 0 (one computing layer and three
+ *             reusing layers per group of four)
+ *  GLM52    : layers 0 and 1, then 2, 6, 10, ... (every fourth from 2); for
+ *             78 layers that is 21 full and 57 reusing layers
+ *  ALL_FULL : every layer (IndexShare off)
+ *  MASK     : full_mask[l] != 0 (host array of n_layers bytes)
+ * Layer 0 must be full. */
+typedef enum {
+  LCS_SCHED_GROUP4 = 0,
+  LCS_SCHED_GLM52 = 1,
+  LCS_SCHED_ALL_FULL = 2,
+  LCS_SCHED_MASK = 3
+} lcs_sched;
+
+/* Number of layers that run their own indexer (the leading dimension of
+ * idx_out), or -1 for invalid arguments. mtp_steps > 0 gives 1. */
+int32_t lcs_count_full_layers(lcs_sched sched, int32_t n_layers,
+                              const uint8_t* full_mask, int32_t mtp_steps);
+
+/* Workspace bytes needed by lcs_indexshare_forward for these sizes. */
+size_t lcs_indexshare_workspace_bytes(int32_t B, int32_t T, int32_t L, int32_t k);
+
+/* The whole path over n_layers layers (layers is a HOST array). For each
+ * layer in order: a full layer runs lcs_idx_score into scores_scratch
+ * [B][T][L] and lcs_topk_select into the next slot of idx_out
+ * [n_full][B][T][k]; every layer then runs lcs_sparse_mla_attn with the
+ * latest full layer's selection. mtp_steps > 0 (MTP draft reuse): layers[]
+ * holds mtp_steps draft steps of one layer; step 0 runs the indexer, and
+ * every step attends with step 0's selection over step 0's kv/kv_scale (KV
+ * Share), each with its own q, out and lse. */
+lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers,
+                                  lcs_sched sched, const uint8_t* full_mask,
+                                  int32_t mtp_steps, lcs_kv_dtype kv_dtype,
+                                  const int32_t* vis_len, int32_t B, int32_t T,
+                                  int32_t L, int32_t k, float sm_scale,
+                                  float* scores_scratch, int32_t* idx_out,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* Static description of a status code. */
+const char* lcs_status_string(lcs_status s);
+/* Thread-local detail of this thread's last failed call ("" if none). */
+const char* lcs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

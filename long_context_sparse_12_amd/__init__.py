@@ -1,0 +1,163 @@
+"""Python binding of liblcs.so, the gfx950 DSA + IndexShare attention path.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/lcs.h. PyTorch supplies device memory and the current
+stream. Importing fails loudly if the library has not been built; there is no
+fallback implementation.
+"""
+import ctypes
+import os
+
+# torch first: its HIP runtime (soname libamdhip64.so.7) is then the one the
+# process uses, and liblcs.so binds to it instead of loading a second runtime
+import torch  # noqa: F401
+
+__all__ = [
+    "LcsError", "idx_score", "topk_workspace_bytes", "topk_select", "attn_workspace_bytes",
+    "sparse_mla_attn", "count_full_layers", "indexshare_workspace_bytes", "indexshare_forward",
+    "SCHED_GROUP4", "SCHED_GLM52", "SCHED_ALL_FULL", "SCHED_MASK", "KV_BF16", "KV_FP8_E4M3",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblcs.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError("%s is missing: run __graft_entry__.build() first" % LIB_PATH)
+_lib = ctypes.CDLL(LIB_PATH)
+
+SCHED_GROUP4, SCHED_GLM52, SCHED_ALL_FULL, SCHED_MASK = 0, 1, 2, 3
+KV_BF16, KV_FP8_E4M3 = 0, 1
+IDX_HEADS, IDX_DIM, ATT_HEADS, KV_LATENT, KV_DIM = 32, 128, 64, 512, 576
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+_f32 = ctypes.c_float
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("q8", "q_scale", "w", "k8", "k_scale", "q", "kv", "kv_scale",
+                                  "out", "lse")]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_c_idx_score = _sig("lcs_idx_score", ctypes.c_int, [_p] * 6 + [_i32] * 3 + [_p, _p])
+_c_topk_ws = _sig("lcs_topk_workspace_bytes", _sz, [_i32] * 4)
+_c_topk = _sig("lcs_topk_select", ctypes.c_int, [_p, _p] + [_i32] * 4 + [_p, _p, _sz, _p])
+_c_attn_ws = _sig("lcs_attn_workspace_bytes", _sz, [_i32] * 3)
+_c_attn = _sig("lcs_sparse_mla_attn", ctypes.c_int,
+               [_p, _p, ctypes.c_int, _p, _p] + [_i32] * 4 + [_f32, _p, _p, _p, _sz, _p])
+_c_count = _sig("lcs_count_full_layers", _i32, [ctypes.c_int, _i32, _p, _i32])
+_c_is_ws = _sig("lcs_indexshare_workspace_bytes", _sz, [_i32] * 4)
+_c_is = _sig("lcs_indexshare_forward", ctypes.c_int,
+             [ctypes.POINTER(_Layer), _i32, ctypes.c_int, _p, _i32, ctypes.c_int, _p]
+             + [_i32] * 4 + [_f32, _p, _p, _p, _sz, _p])
+_c_status = _sig("lcs_status_string", ctypes.c_char_p, [ctypes.c_int])
+_c_last = _sig("lcs_last_error", ctypes.c_char_p, [])
+
+
+class LcsError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__("lcs status %d (%s): %s" % (status, _c_status(status).decode(), detail))
+
+
+def _check(rc):
+    if rc != 0:
+        raise LcsError(rc, _c_last().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def idx_score(q8, q_scale, w, k8, k_scale, vis_len, scores, stream=None):
+    """scores[B,T,L] (fp32) from q8[B,T,32,128], q_scale/w[B,T,32], k8[B,L,128],
+    k_scale[B,L], vis_len[B,T] (int32)."""
+    B, T = q8.shape[0], q8.shape[1]
+    L = k8.shape[1]
+    _check(_c_idx_score(_ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8), _ptr(k_scale),
+                        _ptr(vis_len), B, T, L, _ptr(scores), _stream(stream)))
+
+
+def topk_workspace_bytes(B, T, L, k):
+    return int(_c_topk_ws(B, T, L, k))
+
+
+def topk_select(scores, vis_len, k, idx, workspace, stream=None):
+    """idx[B,T,k] (int32) from scores[B,T,L]; workspace: uint8 device tensor of at least
+    topk_workspace_bytes(B, T, L, k) bytes."""
+    B, T, L = scores.shape
+    _check(_c_topk(_ptr(scores), _ptr(vis_len), B, T, L, k, _ptr(idx), _ptr(workspace),
+                   0 if workspace is None else workspace.numel() * workspace.element_size(),
+                   _stream(stream)))
+
+
+def attn_workspace_bytes(B, T, k):
+    return int(_c_attn_ws(B, T, k))
+
+
+def _kv_dtype(kv):
+    import torch
+    if kv.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return KV_FP8_E4M3
+    return KV_BF16
+
+
+def sparse_mla_attn(q, kv, kv_scale, idx, sm_scale, out, lse=None, workspace=None, stream=None):
+    """out[B,T,64,512] (bf16) from q[B,T,64,576] (bf16), kv[B,L,576] (bf16, or uint8 E4M3
+    codes with kv_scale[B,L]), idx[B,T,k]."""
+    B, T = q.shape[0], q.shape[1]
+    L = kv.shape[1]
+    k = idx.shape[-1]
+    _check(_c_attn(_ptr(q), _ptr(kv), _kv_dtype(kv), _ptr(kv_scale), _ptr(idx), B, T, L, k,
+                   float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                   0 if workspace is None else workspace.numel() * workspace.element_size(),
+                   _stream(stream)))
+
+
+def count_full_layers(sched, n_layers, full_mask=None, mtp_steps=0):
+    buf = None
+    if full_mask is not None:
+        buf = (ctypes.c_uint8 * n_layers)(*[1 if x else 0 for x in full_mask])
+    n = _c_count(sched, n_layers, ctypes.cast(buf, _p) if buf is not None else None, mtp_steps)
+    if n < 0:
+        raise ValueError("invalid schedule arguments")
+    return int(n)
+
+
+def indexshare_workspace_bytes(B, T, L, k):
+    return int(_c_is_ws(B, T, L, k))
+
+
+def indexshare_forward(layers, sched, vis_len, k, sm_scale, scores_scratch, idx_out, workspace,
+                       kv_dtype=KV_BF16, mtp_steps=0, full_mask=None, stream=None):
+    """layers: list of dicts with keys q8, q_scale, w, k8, k_scale (full layers), q, kv,
+    kv_scale, out, lse (tensors or None). Shapes as in the single calls."""
+    n = len(layers)
+    arr = (_Layer * n)()
+    for i, ly in enumerate(layers):
+        for f, _ in _Layer._fields_:
+            setattr(arr[i], f, _ptr(ly.get(f)))
+    B, T = vis_len.shape
+    L = scores_scratch.shape[-1]
+    buf = None
+    if full_mask is not None:
+        buf = (ctypes.c_uint8 * n)(*[1 if x else 0 for x in full_mask])
+    _check(_c_is(arr, n, sched, ctypes.cast(buf, _p) if buf is not None else None, mtp_steps,
+                 kv_dtype, _ptr(vis_len), B, T, L, k, float(sm_scale), _ptr(scores_scratch),
+                 _ptr(idx_out), _ptr(workspace),
+                 workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                 _stream(stream)))

@@ -1,0 +1,87 @@
+// common.h -- shared device helpers and launcher declarations of the gfx950
+// DSA + IndexShare kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace lcs {
+
+// Launch through hipLaunchKernel, which returns this launch's own status (the
+// per-thread sticky error of hipGetLastError may hold an unrelated earlier
+// failure of the caller's HIP calls).
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<KArgs...> vals(static_cast<KArgs>(args)...);
+  void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = (void*)&v), ...);
+  }, vals);
+  return hipLaunchKernel((const void*)kernel, grid, block, ptrs, shmem, stream);
+}
+
+
+constexpr int kIdxHeads = 32;
+constexpr int kIdxDim = 128;
+constexpr int kAttHeads = 64;
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kKvDim = kLatent + kRope;  // 576
+constexpr int kMaxTopk = 2048;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Order-preserving map of an fp32 score onto uint32: a larger float gives a
+// larger key. -0.0 is folded onto +0.0 so that equal scores give equal keys.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int clamp_vis(int v, int L) { return v < 0 ? 0 : (v > L ? L : v); }
+
+// two fp32 -> packed bf16 pair, round to nearest even
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+  a += 0x7FFFu + ((a >> 16) & 1u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t a = __float_as_uint(f);
+  a += 0x7FFFu + ((a >> 16) & 1u);
+  return (uint16_t)(a >> 16);
+}
+
+// ---- launchers (host) ----
+
+hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
+                            const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
+                            int B, int T, int L, float* scores, hipStream_t stream);
+
+size_t topk_workspace_bytes(int64_t rows, int L, int k);
+hipError_t launch_topk(const float* scores, const int32_t* vis_len, int rows, int L, int k,
+                       int32_t* idx, void* workspace, hipStream_t stream);
+
+size_t attn_workspace_bytes(int64_t queries, int k);
+hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
+                             const float* kv_scale, const int32_t* idx, int B, int T, int L,
+                             int k, float sm_scale, uint16_t* out, float* lse,
+                             void* workspace, hipStream_t stream);
+
+}  // namespace lcs

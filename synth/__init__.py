@@ -36,6 +36,7 @@ _dev = None
 def _devlib():
     global _dev
     if _dev is None:
+        import torch  # noqa: F401  (one HIP runtime per process: torch's, loaded first)
         _dev = ctypes.CDLL(os.path.join(HERE, "libsynth_dev.so"))
         _dev.synth_dev_fp8_rows.argtypes = [_u64, _u32, _u32, _i64, _i32, _u32, _i32, _i32, _i64,
                                             _i64, _p, _p, _p]

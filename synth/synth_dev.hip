@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
+
+#include <tuple>
 
 #define SYN_FN __host__ __device__ static inline
 #include "synth.h"
@@ -79,6 +82,23 @@ __global__ void __launch_bounds__(256) uniform_rows_kernel(
   }
 }
 
+// hipLaunchKernel returns this launch's own status
+template <typename... KArgs, typename... Args>
+int launch(const char* what, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+           Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<KArgs...> vals(static_cast<KArgs>(args)...);
+  void* ptrs[sizeof...(KArgs)];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = (void*)&v), ...);
+  }, vals);
+  const hipError_t e = hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, stream);
+  if (e == hipSuccess) return 0;
+  fprintf(stderr, "synth %s: %s\n", what, hipGetErrorString(e));
+  return 2;
+}
+
 int grid_for(int64_t work, int per_block) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g > 65536) g = 65536;
@@ -96,10 +116,8 @@ int synth_dev_fp8_rows(uint64_t seed, uint32_t tensor, uint32_t layer, int64_t R
                        hipStream_t stream) {
   if (D <= 0 || D > 64 * kMaxPerLane || nb < 0 || nr < 0 || !codes || !scales) return 1;
   if ((int64_t)nb * nr == 0) return 0;
-  hipLaunchKernelGGL(fp8_rows_kernel, dim3(grid_for((int64_t)nb * nr, 4)), dim3(256), 0,
-                     stream, seed, tensor, layer, R, D, plant_permyriad, b0, nb, r0, nr,
-                     codes, scales);
-  return hipGetLastError() == hipSuccess ? 0 : 2;
+  return launch("fp8 rows", fp8_rows_kernel, dim3(grid_for((int64_t)nb * nr, 4)), dim3(256),
+                stream, seed, tensor, layer, R, D, plant_permyriad, b0, nb, r0, nr, codes, scales);
 }
 
 int synth_dev_bf16_rows(uint64_t seed, uint32_t tensor, uint32_t layer, int32_t D,
@@ -108,9 +126,8 @@ int synth_dev_bf16_rows(uint64_t seed, uint32_t tensor, uint32_t layer, int32_t 
   if (D <= 0 || nb < 0 || nr < 0 || !out) return 1;
   const int64_t total = (int64_t)nb * nr * D;
   if (total == 0) return 0;
-  hipLaunchKernelGGL(bf16_rows_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
-                     seed, tensor, layer, D, b0, nr, r0, total, out);
-  return hipGetLastError() == hipSuccess ? 0 : 2;
+  return launch("bf16 rows", bf16_rows_kernel, dim3(grid_for(total, 256)), dim3(256), stream,
+                seed, tensor, layer, D, b0, nr, r0, total, out);
 }
 
 int synth_dev_uniform_rows(uint64_t seed, uint32_t tensor, uint32_t layer, int32_t D,
@@ -119,9 +136,8 @@ int synth_dev_uniform_rows(uint64_t seed, uint32_t tensor, uint32_t layer, int32
   if (D <= 0 || nb < 0 || nr < 0 || !out) return 1;
   const int64_t total = (int64_t)nb * nr * D;
   if (total == 0) return 0;
-  hipLaunchKernelGGL(uniform_rows_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
-                     seed, tensor, layer, D, b0, nr, r0, total, out);
-  return hipGetLastError() == hipSuccess ? 0 : 2;
+  return launch("uniform rows", uniform_rows_kernel, dim3(grid_for(total, 256)), dim3(256), stream,
+                seed, tensor, layer, D, b0, nr, r0, total, out);
 }
 
 }  // extern "C"

@@ -1,0 +1,48 @@
+"""One small decode pass of the whole path on cuda:0, checked against the oracle:
+the tiny IndexShare group (1 x 4 queries, L = 8192, layer 0 full, layers 1-3
+reuse its top-2048)."""
+import numpy as np
+import torch
+
+import long_context_sparse_12_amd as lcs
+import oracle
+from synth import workloads as wl
+from tests.parity import DEV, check_attention, check_selection, to_dev
+
+
+def run_smoke():
+    w = wl.WORKLOADS["tiny"]
+    B, T, L, k = w.B, w.T, w.L, w.k
+    vis = w.vis_len()
+    layers_h = []
+    for l in range(w.n_layers):
+        ly = wl.host_indexer(w, l) if l in w.full_layers() else {}
+        ly["q"] = wl.host_attn_q(w, l)
+        ly["kv"], _ = wl.host_kv(w, l)
+        layers_h.append(ly)
+    layers_d = []
+    for ly in layers_h:
+        d = {f: to_dev(a) for f, a in ly.items()}
+        d["out"] = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+        d["lse"] = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+        layers_d.append(d)
+    idx_out = torch.empty((1, B, T, k), dtype=torch.int32, device=DEV)
+    scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(lcs.indexshare_workspace_bytes(B, T, L, k), dtype=torch.uint8, device=DEV)
+    lcs.indexshare_forward(layers_d, lcs.SCHED_GROUP4, to_dev(vis), k, w.sm_scale, scores,
+                           idx_out, ws)
+    torch.cuda.synchronize()
+    outs, lses, ref_idx = oracle.indexshare(layers_h, oracle.SCHED_GROUP4, vis, k, w.sm_scale)
+    _, s64 = oracle.idx_score(layers_h[0]["q8"], layers_h[0]["q_scale"], layers_h[0]["w"],
+                              layers_h[0]["k8"], layers_h[0]["k_scale"], vis, want64=True)
+    overlap, gap = check_selection(idx_out[0].cpu().numpy(), ref_idx[0], s64)
+    worst = 0.0
+    if np.array_equal(idx_out[0].cpu().numpy(), ref_idx[0]):
+        for l in range(w.n_layers):
+            _, _, o64 = oracle.sparse_mla(layers_h[l]["q"], layers_h[l]["kv"], None, ref_idx[0],
+                                          w.sm_scale, want64=True)
+            mx, _, _ = check_attention(layers_d[l]["out"], o64, layers_d[l]["lse"],
+                                       lses[l].astype(np.float64))
+            worst = max(worst, mx)
+    print("smoke ok: %s, selection overlap %.5f (worst gap %.2g), attention max-abs %.3g"
+          % (w.name, overlap, gap, worst), flush=True)

@@ -1,0 +1,132 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/lcs.h declares, sizes workspaces, counts schedule layers and rejects
+bad arguments on the host before any launch (every call here fails
+validation, so nothing reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_12_amd as lcs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "lcs.h")
+lib = ctypes.CDLL(lcs.LIB_PATH)
+
+OK, NULL, SHAPE, UNSUP, WS, HIP = 0, 1, 2, 3, 4, 5
+P = 0x100000  # fake 16-byte-aligned address: never dereferenced, validation fails first
+_v, _i, _z, _f = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+
+
+def _declared():
+    text = re.sub(r"/\*.*?\*/", "", open(HDR).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(lcs_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = _declared()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _fn(name, args, res=ctypes.c_int):
+    f = getattr(lib, name)
+    f.argtypes, f.restype = args, res
+    return f
+
+
+idx_score = _fn("lcs_idx_score", [_v] * 6 + [_i] * 3 + [_v, _v])
+topk = _fn("lcs_topk_select", [_v, _v] + [_i] * 4 + [_v, _v, _z, _v])
+attn = _fn("lcs_sparse_mla_attn", [_v, _v, ctypes.c_int, _v, _v] + [_i] * 4 + [_f, _v, _v, _v, _z, _v])
+last = _fn("lcs_last_error", [], ctypes.c_char_p)
+
+
+def test_idx_score_validation():
+    assert idx_score(None, P, P, P, P, P, 1, 1, 64, P, None) == NULL
+    assert b"q8" in last()
+    assert idx_score(P + 4, P, P, P, P, P, 1, 1, 64, P, None) == SHAPE
+    assert idx_score(P, P, P, P, P, P, 0, 1, 64, P, None) == SHAPE
+    assert idx_score(P, P, P, P, P, P, 1, 1, -5, P, None) == SHAPE
+    assert idx_score(P, P, P, P, P, P, 1, 1, (1 << 30) + 1, P, None) == SHAPE
+    assert idx_score(P, P, P, P, P, None, 1, 1, 64, P, None) == NULL
+
+
+def test_topk_validation():
+    need = lcs.topk_workspace_bytes(2, 1, 131072, 2048)
+    assert need > 2 * 131072 * 4
+    assert topk(P, P, 2, 1, 131072, 0, P, P, need, None) == UNSUP
+    assert topk(P, P, 2, 1, 131072, 2049, P, P, need, None) == UNSUP
+    assert topk(P, P, 2, 1, 131072, 2048, P, None, need, None) == WS
+    assert topk(P, P, 2, 1, 131072, 2048, P, P, need - 1, None) == WS
+    assert b"needed" in last()
+    assert topk(P, P, 2, 1, 131072, 2048, None, P, need, None) == NULL
+    assert topk(P, P, 2, 0, 131072, 2048, P, P, need, None) == SHAPE
+
+
+def test_attn_validation():
+    need = lcs.attn_workspace_bytes(2, 1, 2048)
+    assert need > 0  # few queries -> split over the selection -> partials
+    assert lcs.attn_workspace_bytes(4096, 1, 2048) == 0  # one split per query
+    args = dict(q=P, kv=P, dt=0, sc=None, idx=P, B=2, T=1, L=1000, k=2048, sm=1 / 24, out=P,
+                lse=None, ws=P, wsb=need)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return attn(a["q"], a["kv"], a["dt"], a["sc"], a["idx"], a["B"], a["T"], a["L"], a["k"],
+                    a["sm"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+    assert call(q=None) == NULL
+    assert call(dt=7) == UNSUP
+    assert call(dt=0, sc=P) == SHAPE  # bf16 takes no scale
+    assert call(dt=1, sc=None) == NULL  # FP8 needs one
+    assert call(sm=0.0) == SHAPE and call(sm=float("nan")) == SHAPE
+    assert call(k=4096) == UNSUP
+    assert call(ws=None) == WS and call(wsb=need - 16) == WS
+    assert call(lse=P + 8) == SHAPE
+
+
+def test_schedules_and_counts():
+    assert lcs.count_full_layers(lcs.SCHED_GLM52, 78) == 21
+    assert lcs.count_full_layers(lcs.SCHED_GROUP4, 4) == 1
+    assert lcs.count_full_layers(lcs.SCHED_GROUP4, 78) == 20
+    assert lcs.count_full_layers(lcs.SCHED_ALL_FULL, 78) == 78
+    assert lcs.count_full_layers(lcs.SCHED_MASK, 5, [1, 0, 1, 1, 0]) == 3
+    assert lcs.count_full_layers(lcs.SCHED_GROUP4, 7, mtp_steps=7) == 1
+    with pytest.raises(ValueError):
+        lcs.count_full_layers(lcs.SCHED_GROUP4, 7, mtp_steps=3)
+    with pytest.raises(ValueError):
+        lcs.count_full_layers(9, 4)
+
+
+def test_indexshare_validation():
+    f = _fn("lcs_indexshare_forward", [_v, _i, ctypes.c_int, _v, _i, ctypes.c_int, _v] + [_i] * 4
+            + [_f, _v, _v, _v, _z, _v])
+    L = lcs._Layer
+    B, T, Ln, k = 1, 1, 4096, 2048
+    need = lcs.indexshare_workspace_bytes(B, T, Ln, k)
+    arr = (L * 4)()
+    for i in range(4):
+        for name, _ in L._fields_:
+            setattr(arr[i], name, P)
+        arr[i].kv_scale = None
+    arr[2].out = None
+    mask = (ctypes.c_uint8 * 4)(0, 1, 1, 1)
+    assert f(None, 4, 0, None, 0, 0, P, B, T, Ln, k, 1 / 24, P, P, P, need, None) == NULL
+    assert f(arr, 4, 3, ctypes.cast(mask, _v), 0, 0, P, B, T, Ln, k, 1 / 24, P, P, P, need,
+             None) == SHAPE  # layer 0 must be full
+    assert f(arr, 4, 0, None, 3, 0, P, B, T, Ln, k, 1 / 24, P, P, P, need, None) == SHAPE
+    assert f(arr, 4, 0, None, 0, 0, P, B, T, Ln, k, 1 / 24, P, P, P, need - 1, None) == WS
+    assert f(arr, 4, 0, None, 0, 0, P, B, T, Ln, k, 1 / 24, P, P, P, need, None) == NULL
+    assert b"layer 2" in last()  # every layer is validated before anything launches
+    assert f(arr, 4, 5, None, 0, 0, P, B, T, Ln, k, 1 / 24, P, P, P, need, None) == UNSUP
+
+
+def test_status_strings():
+    f = _fn("lcs_status_string", [ctypes.c_int], ctypes.c_char_p)
+    assert f(0) == b"ok" and f(4) == b"workspace missing or too small" and f(99) == b"unknown status"
+    with pytest.raises(lcs.LcsError) as e:
+        lcs._check(WS)
+    assert e.value.status == WS

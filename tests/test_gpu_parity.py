@@ -1,0 +1,319 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle, at
+sizes the oracle finishes in seconds: several tiles, ragged tails, edge cases.
+Expected values always come from the oracle run on host-generated inputs."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_12_amd as lcs
+import oracle
+import synth
+from synth import workloads as wl
+from tests.parity import (DEV, bf16_to_f64, check_attention, check_scores, check_selection,
+                          to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _zeros(nbytes):
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=DEV)
+
+
+# ------------------------------------------------------------------ generator
+def test_device_generator_matches_host():
+    _say("case: generator device vs host")
+    for tensor, R, D, perm, b0, nb, r0, nr in [(synth.T_IDX_KEY, 5000, 128, 100, 1, 2, 1000, 777),
+                                               (synth.T_KV, 300, 576, 0, 0, 1, 0, 300),
+                                               (synth.T_IDX_Q, 128, 128, 0, 3, 1, 0, 128)]:
+        ch, sh = synth.host_fp8_rows(11, tensor, 3, R, D, perm, b0, nb, r0, nr)
+        cd = torch.empty(nb * nr * D, dtype=torch.uint8, device=DEV)
+        sd = torch.empty(nb * nr, dtype=torch.float32, device=DEV)
+        synth.dev_fp8_rows(11, tensor, 3, R, D, perm, b0, nb, r0, nr, cd, sd)
+        assert np.array_equal(cd.cpu().numpy(), ch.ravel())
+        assert np.array_equal(sd.cpu().numpy().view(np.uint32), sh.ravel().view(np.uint32))
+    bh = synth.host_bf16_rows(12, synth.T_ATT_Q, 2, 576, 1, 2, 5, 70)
+    bd = torch.empty(2 * 70 * 576, dtype=torch.bfloat16, device=DEV)
+    synth.dev_bf16_rows(12, synth.T_ATT_Q, 2, 576, 1, 2, 5, 70, bd)
+    assert np.array_equal(bd.view(torch.int16).cpu().numpy().view(np.uint16), bh.ravel())
+    uh = synth.host_uniform_rows(13, synth.T_IDX_W, 1, 32, 0, 3, 0, 9)
+    ud = torch.empty(3 * 9 * 32, dtype=torch.float32, device=DEV)
+    synth.dev_uniform_rows(13, synth.T_IDX_W, 1, 32, 0, 3, 0, 9, ud)
+    assert np.array_equal(ud.cpu().numpy().view(np.uint32), uh.ravel().view(np.uint32))
+
+
+# ------------------------------------------------------------------ indexer
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8])
+def test_idx_score_matches_oracle(T):
+    _say("case: idx_score T=%d" % T)
+    B, L = 2, 8192 + 37
+    w = wl.Workload("idx-parity", seed=40 + T, B=B, T=T, L=L, n_layers=1, plant_permyriad=100)
+    inp = wl.host_indexer(w, 0)
+    rs = np.random.default_rng(T)
+    vis = rs.integers(L - 300, L + 1, size=(B, T)).astype(np.int32)
+    vis[0, 0] = L
+    if T > 1:
+        vis[1, 1] = 100
+    _, ref64 = oracle.idx_score(inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"],
+                                vis, want64=True)
+    scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+    lcs.idx_score(to_dev(inp["q8"]), to_dev(inp["q_scale"]), to_dev(inp["w"]), to_dev(inp["k8"]),
+                  to_dev(inp["k_scale"]), to_dev(vis), scores)
+    rel = check_scores(scores.cpu().numpy(), ref64)
+    _say("  max rel err %.3g" % rel)
+
+
+# ------------------------------------------------------------------ top-k
+def _topk_case(name, B, T, L, k, seed):
+    rs = np.random.default_rng(seed)
+    vis = np.full((B, T), L, np.int32)
+    if name == "normal":
+        s = rs.standard_normal((B, T, L)).astype(np.float32)
+    elif name == "ties":
+        s = (rs.integers(0, 300, size=(B, T, L)) * 0.5).astype(np.float32)
+    elif name == "equal":
+        s = np.full((B, T, L), 3.0, np.float32)
+    elif name == "ragged":
+        s = rs.standard_normal((B, T, L)).astype(np.float32) * 100
+        vis = rs.integers(0, L + 1, size=(B, T)).astype(np.int32)
+        vis.flat[0] = 0
+        vis.flat[-1] = min(L, k - 1) if L >= 1 else 0
+        if vis.size > 2:
+            vis.flat[1] = min(L, k)
+            vis.flat[2] = min(L, k + 1)
+    elif name == "signed-zero":
+        s = rs.choice(np.array([-0.0, 0.0, 1.0, -1.0], np.float32), size=(B, T, L))
+    elif name == "planted":
+        s = np.abs(rs.standard_normal((B, T, L))).astype(np.float32) * 70
+        s[..., rs.choice(L, 1311, replace=False)] += 200
+    else:
+        raise ValueError(name)
+    return s, vis
+
+
+TOPK_CASES = [
+    ("normal", 1, 4, 8192, 2048), ("ragged", 2, 3, 8192 + 37, 2048), ("ties", 1, 2, 20000, 2048),
+    ("equal", 1, 1, 10000, 2048), ("normal", 3, 1, 5000, 64), ("signed-zero", 1, 2, 9000, 1000),
+    ("normal", 1, 2, 131072, 2048), ("planted", 2, 1, 131072, 2048), ("normal", 1, 300, 4001, 2048),
+    ("ragged", 1, 5, 3001, 2048), ("normal", 1, 1, 1 << 20, 2048), ("ties", 1, 1, 1 << 20, 2048),
+    ("normal", 2, 2, 1, 1), ("normal", 1, 1, 2048, 2048),
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=lambda c: "%s-B%d-T%d-L%d-k%d" % c)
+def test_topk_bit_exact_on_oracle_scores(case):
+    name, B, T, L, k = case
+    _say("case: topk %s B=%d T=%d L=%d k=%d" % case)
+    s, vis = _topk_case(name, B, T, L, k, seed=B * 1000 + T * 10 + L % 97)
+    ref = oracle.topk(s, vis, k)
+    ds, dv = to_dev(s), to_dev(vis)
+    idx = torch.full((B, T, k), -7, dtype=torch.int32, device=DEV)
+    ws = _zeros(lcs.topk_workspace_bytes(B, T, L, k))
+    lcs.topk_select(ds, dv, k, idx, ws)
+    got = idx.cpu().numpy()
+    bad = np.argwhere(np.any(got != ref, axis=-1))
+    assert bad.size == 0, "rows differ: %s" % bad[:5].tolist()
+    # the call restores the workspace's counters and histograms, so a second call on the
+    # same workspace reproduces the result
+    idx2 = torch.full((B, T, k), -9, dtype=torch.int32, device=DEV)
+    lcs.topk_select(ds, dv, k, idx2, ws)
+    assert torch.equal(idx, idx2)
+
+
+def test_topk_workspace_reused_across_shapes():
+    _say("case: topk workspace reuse")
+    shapes = [(1, 1, 1 << 20, 2048), (4, 8, 30000, 2048), (1, 3, 7000, 512)]
+    ws = _zeros(max(lcs.topk_workspace_bytes(*sh) for sh in shapes))
+    for rep in range(2):
+        for (B, T, L, k) in shapes:
+            s, vis = _topk_case("ragged" if rep else "normal", B, T, L, k, seed=L + rep)
+            idx = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+            lcs.topk_select(to_dev(s), to_dev(vis), k, idx, ws)
+            assert np.array_equal(idx.cpu().numpy(), oracle.topk(s, vis, k))
+
+
+# ------------------------------------------------------------------ attention
+def _attn_inputs(B, T, L, k, fp8, seed, pad=0, peak=False):
+    rs = np.random.default_rng(seed)
+    w = wl.Workload("attn-parity", seed=seed, B=B, T=T, L=L, n_layers=1, kv_fp8=fp8)
+    q = wl.host_attn_q(w, 0)
+    kv, sc = wl.host_kv(w, 0)
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            m = min(k - pad, L)
+            idx[b, t, :m] = np.sort(rs.choice(L, m, replace=False))
+    if peak:
+        # every head's query points at the first selected row with logit 20, so the
+        # output is close to that row: unit-scale outputs, where 2e-2 is tight
+        for b in range(B):
+            for t in range(T):
+                s = idx[b, t, 0]
+                if fp8:
+                    r = np.array([oracle.e4m3(c) for c in kv[b, s]]) * float(sc[b, s])
+                else:
+                    r = bf16_to_f64(kv[b, s])
+                qv = (r * (20.0 * 24.0 / np.dot(r, r))).astype(np.float32)
+                q[b, t, :] = torch.from_numpy(qv).to(torch.bfloat16).view(torch.int16).numpy().view(
+                    np.uint16)
+    return q, kv, sc, idx
+
+
+ATTN_CASES = [
+    (1, 4, 8192, 2048, False, 0, False), (2, 3, 5000, 2048, True, 100, False),
+    (40, 1, 3000, 2048, False, 0, False), (1, 1, 500, 100, False, 0, False),
+    (300, 1, 4096, 2048, False, 7, False), (2, 1, 3000, 2048, False, 0, True), (2, 2, 3000, 1024, True, 0, True),
+    (8, 1, 6000, 2048, True, 0, False), (1, 2, 200, 2048, True, 2048 - 200, False),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "B%d-T%d-L%d-k%d-fp8%d-pad%d-peak%d" % c)
+def test_sparse_mla_matches_oracle(case):
+    B, T, L, k, fp8, pad, peak = case
+    _say("case: sparse_mla B=%d T=%d L=%d k=%d fp8=%d pad=%d peak=%d" % case)
+    q, kv, sc, idx = _attn_inputs(B, T, L, k, fp8, seed=B * 7 + T + L % 13, pad=pad, peak=peak)
+    ref_out, ref_lse, ref64 = oracle.sparse_mla(q, kv, sc, idx, 1 / 24, want64=True)
+    out = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+    ws = _zeros(lcs.attn_workspace_bytes(B, T, k))
+    lcs.sparse_mla_attn(to_dev(q), to_dev(kv), None if sc is None else to_dev(sc), to_dev(idx),
+                        1 / 24, out, lse, ws)
+    mx, ratio, lerr = check_attention(out, ref64, lse, ref_lse.astype(np.float64))
+    _say("  max-abs %.3g (%.3g of rms), lse err %.3g" % (mx, ratio, lerr))
+
+
+def test_sparse_mla_empty_selection():
+    _say("case: sparse_mla all -1")
+    q, kv, sc, idx = _attn_inputs(2, 1, 100, 64, False, seed=5)
+    idx[:] = -1
+    idx[1, 0, 10] = 7
+    _, ref_lse, ref64 = oracle.sparse_mla(q, kv, sc, idx, 1 / 24, want64=True)
+    out = torch.empty((2, 1, 64, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((2, 1, 64), dtype=torch.float32, device=DEV)
+    ws = _zeros(lcs.attn_workspace_bytes(2, 1, 64))
+    lcs.sparse_mla_attn(to_dev(q), to_dev(kv), None, to_dev(idx), 1 / 24, out, lse, ws)
+    check_attention(out, ref64, lse, ref_lse.astype(np.float64))
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+# ------------------------------------------------------------------ composite
+def _dev_layers(layers):
+    out = []
+    for ly in layers:
+        d = {}
+        for f, a in ly.items():
+            d[f] = None if a is None else to_dev(a)
+        out.append(d)
+    return out
+
+
+def _run_composite(w, layers_h, sched, mtp_steps=0, mask=None):
+    B, T, L, k = w.B, w.T, w.L, w.k
+    vis = w.vis_len()
+    layers_d = _dev_layers(layers_h)
+    for ly in layers_d:
+        ly["out"] = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+        ly["lse"] = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+    n_full = lcs.count_full_layers(sched, len(layers_h), mask, mtp_steps)
+    idx_out = torch.empty((n_full, B, T, k), dtype=torch.int32, device=DEV)
+    scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+    ws = _zeros(lcs.indexshare_workspace_bytes(B, T, L, k))
+    lcs.indexshare_forward(layers_d, sched, to_dev(vis), k, w.sm_scale, scores, idx_out, ws,
+                           kv_dtype=lcs.KV_FP8_E4M3 if w.kv_fp8 else lcs.KV_BF16,
+                           mtp_steps=mtp_steps, full_mask=mask)
+    torch.cuda.synchronize()
+    return layers_d, idx_out
+
+
+def _host_layers(w, n, full_layers):
+    layers = []
+    for l in range(n):
+        li = w.indexer_layer(l)
+        ly = {}
+        if l in full_layers:
+            ly.update(wl.host_indexer(w, li))
+        ly["q"] = wl.host_attn_q(w, l)
+        kv, sc = wl.host_kv(w, li)
+        ly["kv"] = kv
+        if sc is not None:
+            ly["kv_scale"] = sc
+        layers.append(ly)
+    return layers
+
+
+def _compare_composite(w, layers_h, layers_d, idx_out, sched, mtp_steps=0, mask=None):
+    vis = w.vis_len()
+    outs, lses, ref_idx = oracle.indexshare(layers_h, sched, vis, w.k, w.sm_scale, kv_fp8=w.kv_fp8,
+                                            mtp_steps=mtp_steps, mask=mask)
+    got_idx = idx_out.cpu().numpy()
+    full = w.full_layers() if mask is None else [l for l in range(len(layers_h)) if mask[l]]
+    for f, l in enumerate(full):
+        ly = layers_h[l]
+        _, s64 = oracle.idx_score(ly["q8"], ly["q_scale"], ly["w"], ly["k8"], ly["k_scale"], vis,
+                                  want64=True)
+        ov, gap = check_selection(got_idx[f], ref_idx[f], s64)
+        _say("  full layer %d: overlap %.5f worst gap %.3g" % (l, ov, gap))
+    for l, ly in enumerate(layers_d):
+        f = 0 if mtp_steps else sum(1 for x in full if x <= l) - 1
+        same = np.array_equal(got_idx[f], ref_idx[f])
+        if same:
+            ref = oracle.sparse_mla(layers_h[l]["q"], layers_h[0 if mtp_steps else l]["kv"],
+                                    layers_h[0 if mtp_steps else l].get("kv_scale"), ref_idx[f],
+                                    w.sm_scale, want64=True)
+            check_attention(ly["out"], ref[2], ly["lse"], ref[1].astype(np.float64))
+
+
+def test_indexshare_tiny_group_end_to_end():
+    w = wl.WORKLOADS["tiny"]
+    _say("case: composite %s" % w.name)
+    layers_h = _host_layers(w, w.n_layers, w.full_layers())
+    layers_d, idx_out = _run_composite(w, layers_h, wl.SCHED_GROUP4)
+    _compare_composite(w, layers_h, layers_d, idx_out, wl.SCHED_GROUP4)
+
+
+def test_indexshare_glm52_schedule_small():
+    w = wl.Workload("glm52-small", seed=21, B=2, T=1, L=6000, n_layers=10, sched=wl.SCHED_GLM52,
+                    kv_fp8=True)
+    _say("case: composite %s" % w.name)
+    layers_h = _host_layers(w, w.n_layers, w.full_layers())
+    layers_d, idx_out = _run_composite(w, layers_h, lcs.SCHED_GLM52)
+    assert idx_out.shape[0] == 4  # layers 0, 1, 2, 6
+    _compare_composite(w, layers_h, layers_d, idx_out, lcs.SCHED_GLM52)
+    # a shared layer's output equals a direct call with its full layer's selection
+    for l, f in ((3, 2), (5, 2), (9, 3)):
+        out = torch.empty_like(layers_d[l]["out"])
+        ws = _zeros(lcs.attn_workspace_bytes(w.B, w.T, w.k))
+        lcs.sparse_mla_attn(layers_d[l]["q"], layers_d[l]["kv"], layers_d[l]["kv_scale"],
+                            idx_out[f], w.sm_scale, out, None, ws)
+        assert torch.equal(out, layers_d[l]["out"])
+
+
+def test_mtp_draft_reuse_small():
+    w = wl.Workload("mtp-small", seed=22, B=3, T=1, L=7000, n_layers=7, kv_fp8=True, mtp_steps=7)
+    _say("case: composite %s" % w.name)
+    layers_h = _host_layers(w, 7, [0])
+    layers_d, idx_out = _run_composite(w, layers_h, 0, mtp_steps=7)
+    assert idx_out.shape[0] == 1
+    _compare_composite(w, layers_h, layers_d, idx_out, 0, mtp_steps=7)
+    # same q at every step -> bit-identical outputs (same selection, same KV)
+    for ly in layers_d:
+        ly["q"] = layers_d[0]["q"]
+    layers_d2, _ = _run_composite(w, [dict(layers_h[0], q=layers_h[0]["q"])] +
+                                  [dict(ly, q=layers_h[0]["q"]) for ly in layers_h[1:]], 0,
+                                  mtp_steps=7)
+    for ly in layers_d2[1:]:
+        assert torch.equal(ly["out"], layers_d2[0]["out"])
+
+
+def test_prefill_causal_small():
+    w = wl.Workload("prefill-small", seed=23, B=1, T=40, L=9000, n_layers=4, prefix=9000 - 40)
+    _say("case: composite %s" % w.name)
+    layers_h = _host_layers(w, 4, [0])
+    layers_d, idx_out = _run_composite(w, layers_h, wl.SCHED_GROUP4)
+    _compare_composite(w, layers_h, layers_d, idx_out, wl.SCHED_GROUP4)
