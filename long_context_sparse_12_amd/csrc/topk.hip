@@ -8,22 +8,21 @@
 //
 // Radix select on order-preserving uint32 keys, split over many workgroups
 // per row so that a few long rows (decode at 128K-1M positions) still fill the
-// chip:
-//   1. hist  : every (row, chunk) workgroup builds an LDS histogram of the top
-//              12 key bits and adds it to the row histogram; the last
-//              workgroup of a row finds the bucket b1 that holds the k-th
-//              largest key and the count of keys above it.
-//   2. select: every (row, chunk) workgroup writes, in position order, the
-//              positions whose bucket is above b1 ("sure") or equal to b1
-//              ("candidate") into its slice of the row's list; the last
-//              workgroup of the row resolves the candidates with two more
-//              digits (12 + 8 bits) in LDS, which fixes the exact threshold
-//              key tau and how many of the keys equal to tau are kept (the
-//              lowest positions), then emits the selection in position order.
-// Scores are read twice from HBM/L2 plus one gather per candidate. A small
-// clearing kernel zeroes the row counters (and the row histograms when a row
-// spans several chunks) at the start of every call, so the workspace needs no
-// preparation and may be reused across shapes.
+// chip. Four launches, with no device-scope fences (on this multi-XCD part a
+// fence writes back and invalidates the whole L2, so cross-workgroup hand-offs
+// go through launch boundaries instead):
+//   clear : zero the row histograms (only when a row spans several chunks)
+//   hist  : every (row, chunk) workgroup builds an LDS histogram of the top 12
+//           key bits and adds it to the row histogram
+//   filter: every (row, chunk) workgroup derives from the row histogram the
+//           bucket b1 holding the k-th largest key, then writes, in position
+//           order, the positions whose bucket is above b1 ("sure") or equal to
+//           b1 ("candidate") into its slice of the row's list
+//   final : one workgroup per row resolves the candidates with two more digits
+//           (12 + 8 bits) in LDS, which fixes the exact threshold key tau and
+//           how many keys equal to tau are kept (the lowest positions), then
+//           emits the selection in position order.
+// Scores are read twice plus one gather per candidate.
 #include "common.h"
 
 namespace lcs {
@@ -39,10 +38,9 @@ constexpr uint32_t kAll = 0xFFFFFFFFu;  // state.b1 marker: keep every visible p
 constexpr uint32_t kSure = 0x80000000u;
 
 struct RowState {
-  uint32_t b1;
-  uint32_t n_above;
-  uint32_t hist_done;
-  uint32_t sel_done;
+  uint32_t b1;       // bucket of the k-th largest key, or kAll
+  uint32_t n_above;  // keys in buckets above b1
+  uint32_t pad0, pad1;
 };
 
 struct Layout {
@@ -75,10 +73,6 @@ __host__ __device__ inline Layout make_layout(int64_t rows, int L) {
   off += (size_t)rows * ly.chunks * (size_t)ly.chunk * sizeof(uint32_t);
   ly.total = off;
   return ly;
-}
-
-__device__ __forceinline__ uint32_t atomic_load_u32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Exclusive prefix over the lanes of a wave of small counts c in [0, 7].
@@ -158,213 +152,196 @@ __device__ void select_bucket(const uint32_t* hist, uint32_t need, uint32_t* s_s
 
 __global__ void __launch_bounds__(kThreads) topk_hist_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ vis_len, int L, int k,
-    int chunks, int chunk, RowState* __restrict__ state, uint32_t* __restrict__ ghist) {
+    int chunks, int chunk, uint32_t* __restrict__ ghist) {
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t s_scan[kThreads + kWavesTk];
-  __shared__ uint32_t s_out[2];
-  __shared__ int s_last;
   const int row = blockIdx.y;
   const int tid = threadIdx.x;
   const int vis = clamp_vis(vis_len[row], L);
   const int begin = blockIdx.x * chunk;
   const int end = min(vis, begin + chunk);
+  if (vis <= k || begin >= end) return;
   uint32_t* rh = ghist + (size_t)row * kBins1;
-  if (vis > k && begin < end) {
-    for (int i = tid; i < kBins1; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    const float* srow = scores + (size_t)row * L;
-    for (int s = begin + tid; s < end; s += kThreads)
-      atomicAdd(&hist[score_key(srow[s]) >> 20], 1u);
-    __syncthreads();
-    for (int i = tid; i < kBins1; i += kThreads) {
-      const uint32_t c = hist[i];
-      if (chunks == 1)
-        rh[i] = c;
-      else if (c)
-        atomicAdd(&rh[i], c);
-    }
-  }
-  __threadfence();
+  for (int i = tid; i < kBins1; i += kThreads) hist[i] = 0;
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&state[row].hist_done, 1u) == (uint32_t)(chunks - 1);
+  const float* srow = scores + (size_t)row * L;
+  for (int s = begin + tid; s < end; s += kThreads) atomicAdd(&hist[score_key(srow[s]) >> 20], 1u);
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (vis <= k) {
-    if (tid == 0) {
-      state[row].b1 = kAll;
-      state[row].n_above = 0;
-    }
-    return;
-  }
-  for (int i = tid; i < kBins1; i += kThreads) hist[i] = atomic_load_u32(&rh[i]);
-  __syncthreads();
-  select_bucket<kBins1>(hist, (uint32_t)k, s_scan, s_out);
-  if (tid == 0) {
-    state[row].b1 = s_out[0];
-    state[row].n_above = s_out[1];
+  for (int i = tid; i < kBins1; i += kThreads) {
+    const uint32_t c = hist[i];
+    if (chunks == 1)
+      rh[i] = c;
+    else if (c)
+      atomicAdd(&rh[i], c);
   }
 }
 
-__global__ void __launch_bounds__(kThreads) topk_select_kernel(
+__global__ void __launch_bounds__(kThreads) topk_filter_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ vis_len, int L, int k,
-    int chunks, int chunk, RowState* __restrict__ state, uint32_t* __restrict__ ghist,
+    int chunks, int chunk, RowState* __restrict__ state, const uint32_t* __restrict__ ghist,
     uint32_t* __restrict__ counts, uint32_t* __restrict__ lists, int32_t* __restrict__ idx) {
+  __shared__ uint32_t s_wave[2 * kWavesTk];
+  __shared__ uint32_t hist[kBins1];
+  __shared__ uint32_t s_scan[kThreads + kWavesTk];
+  __shared__ uint32_t s_out[2];
+  const int row = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int vis = clamp_vis(vis_len[row], L);
+  const int begin = blockIdx.x * chunk;
+  const int end = min(vis, begin + chunk);
+  int32_t* out = idx + (size_t)row * k;
+  if (vis <= k) {
+    // every visible position is kept: positions in order, then -1 padding
+    for (int s = begin + tid; s < end; s += kThreads) out[s] = s;
+    if (blockIdx.x == 0) {
+      for (int i = vis + tid; i < k; i += kThreads) out[i] = -1;
+      if (tid == 0) state[row] = RowState{kAll, 0u, 0u, 0u};
+    }
+    return;
+  }
+  // bucket of the k-th largest key from the row histogram
+  const uint32_t* rh = ghist + (size_t)row * kBins1;
+  for (int i = tid; i < kBins1; i += kThreads) hist[i] = rh[i];
+  __syncthreads();
+  select_bucket<kBins1>(hist, (uint32_t)k, s_scan, s_out);
+  const uint32_t b1 = s_out[0];
+  if (blockIdx.x == 0 && tid == 0) state[row] = RowState{b1, s_out[1], 0u, 0u};
+  // ordered compaction of sure / candidate positions of this chunk
+  const float* srow = scores + (size_t)row * L;
+  uint32_t* my = lists + ((size_t)row * chunks + blockIdx.x) * (size_t)chunk;
+  uint32_t written = 0;
+  int parity = 0;
+  for (int base = begin; base < end; base += 4 * kThreads) {
+    uint32_t e[4];
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = base + 4 * tid + j;
+      e[j] = 0;
+      if (s < end) {
+        const uint32_t d = score_key(srow[s]) >> 20;
+        if (d >= b1) {
+          e[j] = (uint32_t)s | (d > b1 ? kSure : 0u) | 0x40000000u;  // bit 30: valid
+          ++c;
+        }
+      }
+    }
+    uint32_t tot;
+    uint32_t pos = written + block_prefix_small(c, s_wave, parity, tot);
+    parity ^= 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (e[j]) my[pos++] = e[j] & ~0x40000000u;
+    written += tot;
+  }
+  if (tid == 0) counts[(size_t)row * chunks + blockIdx.x] = written;
+}
+
+__global__ void __launch_bounds__(kThreads) topk_final_kernel(
+    const float* __restrict__ scores, int L, int k, int chunks, int chunk,
+    const RowState* __restrict__ state, const uint32_t* __restrict__ counts,
+    const uint32_t* __restrict__ lists, int32_t* __restrict__ idx) {
   __shared__ uint32_t s_wave[2 * kWavesTk];
   __shared__ uint32_t hist[kBins2];
   __shared__ uint32_t s_scan[kThreads + kWavesTk];
   __shared__ uint32_t s_out[2];
   __shared__ uint32_t s_pref[1024 + 1];
-  __shared__ int s_last;
-
-  const int row = blockIdx.y;
+  const int row = blockIdx.x;
   const int tid = threadIdx.x;
-  const int vis = clamp_vis(vis_len[row], L);
-  const int begin = blockIdx.x * chunk;
-  const int end = min(vis, begin + chunk);
-  const uint32_t b1 = state[row].b1;
+  const RowState st = state[row];
+  if (st.b1 == kAll) return;
+  const uint32_t b1 = st.b1;
   const float* srow = scores + (size_t)row * L;
   int32_t* out = idx + (size_t)row * k;
-  uint32_t* list = lists + (size_t)row * chunks * (size_t)chunk;
-
-  if (b1 == kAll) {
-    for (int s = begin + tid; s < end; s += kThreads) out[s] = s;
-  } else {
-    // ordered compaction of sure / candidate positions of this chunk
-    uint32_t* my = list + (size_t)blockIdx.x * chunk;
-    uint32_t written = 0;
-    int parity = 0;
-    for (int base = begin; base < end; base += 4 * kThreads) {
-      uint32_t e[4];
-      uint32_t c = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = base + 4 * tid + j;
-        e[j] = 0;
-        if (s < end) {
-          const uint32_t d = score_key(srow[s]) >> 20;
-          if (d >= b1) {
-            e[j] = (uint32_t)s | (d > b1 ? kSure : 0u) | 0x40000000u;  // bit 30: valid
-            ++c;
-          }
-        }
-      }
-      uint32_t tot;
-      uint32_t pos = written + block_prefix_small(c, s_wave, parity, tot);
-      parity ^= 1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (e[j]) my[pos++] = e[j] & ~0x40000000u;
-      written += tot;
+  const uint32_t* list = lists + (size_t)row * chunks * (size_t)chunk;
+  // chunk offsets in the concatenated entry list
+  for (int c = tid; c < chunks; c += kThreads) s_pref[c] = counts[(size_t)row * chunks + c];
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t run = 0;
+    for (int c = 0; c < chunks; ++c) {
+      const uint32_t v = s_pref[c];
+      s_pref[c] = run;
+      run += v;
     }
-    if (tid == 0) counts[(size_t)row * chunks + blockIdx.x] = written;
+    s_pref[chunks] = run;
   }
-  __threadfence();
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&state[row].sel_done, 1u) == (uint32_t)(chunks - 1);
+  const uint32_t n_ent = s_pref[chunks];
+  const uint32_t n_above = st.n_above;
+  auto entry = [&](uint32_t e) -> uint32_t {
+    int lo = 0, hi = chunks - 1;  // last chunk with s_pref[c] <= e
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    return list[(size_t)lo * chunk + (e - s_pref[lo])];
+  };
+  // digit 2 over the candidates
+  for (int i = tid; i < kBins2; i += kThreads) hist[i] = 0;
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // ---- last workgroup of the row: finish the selection ----
-  if (b1 == kAll) {
-    for (int i = vis + tid; i < k; i += kThreads) out[i] = -1;
-  } else {
-    // chunk offsets in the concatenated entry list
-    if (tid == 0) {
-      uint32_t run = 0;
-      for (int c = 0; c < chunks; ++c) {
-        s_pref[c] = run;
-        run += atomic_load_u32(&counts[(size_t)row * chunks + c]);
-      }
-      s_pref[chunks] = run;
+  for (uint32_t e = tid; e < n_ent; e += kThreads) {
+    const uint32_t v = entry(e);
+    if (!(v & kSure)) atomicAdd(&hist[(score_key(srow[v]) >> 8) & 0xFFFu], 1u);
+  }
+  __syncthreads();
+  const uint32_t need1 = (uint32_t)k - n_above;
+  select_bucket<kBins2>(hist, need1, s_scan, s_out);
+  const uint32_t b2 = s_out[0];
+  const uint32_t above2 = s_out[1];
+  __syncthreads();
+  // digit 3 over the candidates inside bucket b2
+  for (int i = tid; i < kBins3; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  const uint32_t pre12 = (b1 << 12) | b2;
+  for (uint32_t e = tid; e < n_ent; e += kThreads) {
+    const uint32_t v = entry(e);
+    if (!(v & kSure)) {
+      const uint32_t key = score_key(srow[v]);
+      if ((key >> 8) == pre12) atomicAdd(&hist[key & 0xFFu], 1u);
     }
-    __syncthreads();
-    const uint32_t n_ent = s_pref[chunks];
-    const uint32_t n_above = state[row].n_above;
-    auto entry = [&](uint32_t e) -> uint32_t {
-      int lo = 0, hi = chunks - 1;  // last chunk with s_pref[c] <= e
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pref[mid] <= e) lo = mid; else hi = mid - 1;
-      }
-      return __hip_atomic_load(&list[(size_t)lo * chunk + (e - s_pref[lo])], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    };
-    // digit 2 over the candidates
-    for (int i = tid; i < kBins2; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    for (uint32_t e = tid; e < n_ent; e += kThreads) {
+  }
+  __syncthreads();
+  const uint32_t need2 = need1 - above2;
+  select_bucket<kBins3>(hist, need2, s_scan, s_out);
+  const uint32_t b3 = s_out[0];
+  const uint32_t above3 = s_out[1];
+  const uint32_t tau = (pre12 << 8) | b3;
+  const uint32_t need_tie = need2 - above3;  // keys equal to tau that are kept
+  __syncthreads();
+  // ordered emission
+  uint32_t ties_before = 0, sel_before = 0;
+  int parity = 0;
+  for (uint32_t base = 0; base < n_ent; base += kThreads) {
+    const uint32_t e = base + tid;
+    uint32_t is_gt = 0, is_tie = 0, s = 0;
+    if (e < n_ent) {
       const uint32_t v = entry(e);
-      if (!(v & kSure)) atomicAdd(&hist[(score_key(srow[v]) >> 8) & 0xFFFu], 1u);
-    }
-    __syncthreads();
-    const uint32_t need1 = (uint32_t)k - n_above;
-    select_bucket<kBins2>(hist, need1, s_scan, s_out);
-    const uint32_t b2 = s_out[0];
-    const uint32_t above2 = s_out[1];
-    __syncthreads();
-    // digit 3 over the candidates inside bucket b2
-    for (int i = tid; i < kBins3; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    const uint32_t pre12 = (b1 << 12) | b2;
-    for (uint32_t e = tid; e < n_ent; e += kThreads) {
-      const uint32_t v = entry(e);
-      if (!(v & kSure)) {
-        const uint32_t key = score_key(srow[v]);
-        if ((key >> 8) == pre12) atomicAdd(&hist[key & 0xFFu], 1u);
+      s = v & ~kSure;
+      if (v & kSure) {
+        is_gt = 1;
+      } else {
+        const uint32_t key = score_key(srow[s]);
+        is_gt = key > tau;
+        is_tie = key == tau;
       }
     }
-    __syncthreads();
-    const uint32_t need2 = need1 - above2;
-    select_bucket<kBins3>(hist, need2, s_scan, s_out);
-    const uint32_t b3 = s_out[0];
-    const uint32_t above3 = s_out[1];
-    const uint32_t tau = (pre12 << 8) | b3;
-    const uint32_t need_tie = need2 - above3;  // keys equal to tau that are kept
-    __syncthreads();
-    // ordered emission
-    uint32_t ties_before = 0, sel_before = 0;
-    int parity = 0;
-    for (uint32_t base = 0; base < n_ent; base += kThreads) {
-      const uint32_t e = base + tid;
-      uint32_t is_gt = 0, is_tie = 0, s = 0;
-      if (e < n_ent) {
-        const uint32_t v = entry(e);
-        s = v & ~kSure;
-        if (v & kSure) {
-          is_gt = 1;
-        } else {
-          const uint32_t key = score_key(srow[s]);
-          is_gt = key > tau;
-          is_tie = key == tau;
-        }
-      }
-      uint32_t tie_tot;
-      const uint32_t tie_rank = ties_before + block_prefix_small(is_tie, s_wave, parity, tie_tot);
-      parity ^= 1;
-      const uint32_t sel = is_gt | (is_tie & (tie_rank < need_tie ? 1u : 0u));
-      uint32_t sel_tot;
-      const uint32_t pos = sel_before + block_prefix_small(sel, s_wave, parity, sel_tot);
-      parity ^= 1;
-      if (sel && pos < (uint32_t)k) out[pos] = (int32_t)s;
-      ties_before += tie_tot;
-      sel_before += sel_tot;
-    }
+    uint32_t tie_tot;
+    const uint32_t tie_rank = ties_before + block_prefix_small(is_tie, s_wave, parity, tie_tot);
+    parity ^= 1;
+    const uint32_t sel = is_gt | (is_tie & (tie_rank < need_tie ? 1u : 0u));
+    uint32_t sel_tot;
+    const uint32_t pos = sel_before + block_prefix_small(sel, s_wave, parity, sel_tot);
+    parity ^= 1;
+    if (sel && pos < (uint32_t)k) out[pos] = (int32_t)s;
+    ties_before += tie_tot;
+    sel_before += sel_tot;
   }
 }
 
-// zero the row counters, and the row histograms when rows span several chunks
-__global__ void __launch_bounds__(256) topk_clear_kernel(RowState* __restrict__ state,
-                                                        uint32_t* __restrict__ ghist, int rows,
-                                                        int chunks) {
-  const int row = blockIdx.x;
-  if (row >= rows) return;
-  if (threadIdx.x == 0) state[row] = RowState{0u, 0u, 0u, 0u};
-  if (chunks > 1) {
-    uint4* h = (uint4*)(ghist + (size_t)row * kBins1);
-    for (int i = threadIdx.x; i < kBins1 / 4; i += blockDim.x) h[i] = uint4{0u, 0u, 0u, 0u};
-  }
+// zero the row histograms (rows that span several chunks accumulate into them)
+__global__ void __launch_bounds__(256) topk_clear_kernel(uint32_t* __restrict__ ghist) {
+  uint4* h = (uint4*)(ghist + (size_t)blockIdx.x * kBins1);
+  for (int i = threadIdx.x; i < kBins1 / 4; i += blockDim.x) h[i] = uint4{0u, 0u, 0u, 0u};
 }
 
 }  // namespace
@@ -382,14 +359,19 @@ hipError_t launch_topk(const float* scores, const int32_t* vis_len, int rows, in
   uint32_t* counts = (uint32_t*)(ws + ly.off_counts);
   uint32_t* lists = (uint32_t*)(ws + ly.off_lists);
   dim3 grid((unsigned)ly.chunks, (unsigned)rows);
-  hipError_t e = launch_kernel(topk_clear_kernel, dim3((unsigned)rows), dim3(256), 0, stream, state,
-                               ghist, rows, ly.chunks);
+  hipError_t e = hipSuccess;
+  if (ly.chunks > 1) {
+    e = launch_kernel(topk_clear_kernel, dim3((unsigned)rows), dim3(256), 0, stream, ghist);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_kernel(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, vis_len, L, k,
+                    ly.chunks, ly.chunk, ghist);
   if (e != hipSuccess) return e;
-  e = launch_kernel(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, vis_len,
-                               L, k, ly.chunks, ly.chunk, state, ghist);
+  e = launch_kernel(topk_filter_kernel, grid, dim3(kThreads), 0, stream, scores, vis_len, L, k,
+                    ly.chunks, ly.chunk, state, ghist, counts, lists, idx);
   if (e != hipSuccess) return e;
-  return launch_kernel(topk_select_kernel, grid, dim3(kThreads), 0, stream, scores, vis_len, L, k,
-                       ly.chunks, ly.chunk, state, ghist, counts, lists, idx);
+  return launch_kernel(topk_final_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores,
+                       L, k, ly.chunks, ly.chunk, state, counts, lists, idx);
 }
 
 }  // namespace lcs
