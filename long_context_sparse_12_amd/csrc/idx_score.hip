@@ -18,6 +18,13 @@
 namespace lcs {
 namespace {
 
+#ifndef LCS_IDX_TARGET_WGS
+#define LCS_IDX_TARGET_WGS 1024
+#endif
+#ifndef LCS_IDX_MAX_ITERS
+#define LCS_IDX_MAX_ITERS 16
+#endif
+
 constexpr int kWaves = 4;
 constexpr int kSuper = 64;  // keys per wave iteration (4 MFMA column tiles of 16)
 
@@ -114,11 +121,11 @@ __global__ void __launch_bounds__(256) idx_decode_kernel(
 hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
                             const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
                             int B, int T, int L, float* scores, hipStream_t stream) {
-  // keys per workgroup: a multiple of 4 waves x 64 keys, sized for >= ~1024 WGs
+  // keys per workgroup: a multiple of 4 waves x 64 keys, sized for enough WGs
   const int64_t total_keys = (int64_t)B * L;
-  int64_t iters = total_keys / (1024LL * kWaves * kSuper);
+  int64_t iters = total_keys / ((int64_t)LCS_IDX_TARGET_WGS * kWaves * kSuper);
   if (iters < 1) iters = 1;
-  if (iters > 16) iters = 16;
+  if (iters > LCS_IDX_MAX_ITERS) iters = LCS_IDX_MAX_ITERS;
   const int kpw = (int)(iters * kWaves * kSuper);
   dim3 grid((unsigned)((L + kpw - 1) / kpw), (unsigned)B);
   for (int t0 = 0; t0 < T; t0 += 4) {
