@@ -7,12 +7,11 @@
 // queries and keys, each with a per-row dequantisation scale.
 //
 // Decode (T <= 4): every key is read once from HBM; each wave runs the 32
-// heads of a query as the M dimension of v_mfma_f32_16x16x128_f8f6f4 (two
-// 16-head halves) against 16 keys as N, K = the whole 128-dim row, then folds
-// ReLU * (w * q_scale) over its heads, sums across the four lane groups and
-// scales by the key's scale. 132 bytes of HBM traffic per key, no reuse, so
-// the kernel is bound by HBM bandwidth; MFMA keeps the 8192 MACs per key off
-// the vector ALU.
+// heads of a query as the M dimension of v_mfma_f32_32x32x64_f8f6f4 against
+// 32 keys as N, then folds ReLU * (w * q_scale) over its heads and scales by
+// the key's scale. 132 bytes of HBM traffic per key, no reuse, so the kernel
+// is bound by HBM bandwidth; MFMA keeps the 8192 MACs per key off the vector
+// ALU.
 #include "common.h"
 
 namespace lcs {
@@ -26,17 +25,36 @@ namespace {
 #endif
 
 constexpr int kWaves = 4;
-constexpr int kSuper = 64;  // keys per wave iteration (4 MFMA column tiles of 16)
+constexpr int kSuper = 64;  // keys per wave iteration (2 MFMA column blocks of 32)
 
-__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
-  v4f c = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ v16f mfma_fp8_32x32x64(const v8i& a, const v8i& b) {
+  v16f c;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = 0.f;
   // format codes 0/0 = FP8 E4M3 for A and B; zero scale operands select the
   // unscaled instruction
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+__device__ __forceinline__ v16f mfma_fp8_32x32x64_acc(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// sum of a value across the two 32-lane halves (lane l and l^32), VALU only
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One wave = 64 keys per step, as two 32-key column blocks of
+// v_mfma_f32_32x32x64_f8f6f4 (the 32 heads are the M dimension, K = 128 in two
+// halves). Operand layout (A and B alike): lane l holds row/column l&31 and
+// the 32 bytes [64kh + 32(l>>5), +32) of the 128-byte row for K half kh. The
+// result holds, in lane l, key l&31 of the block and heads 8(i/4) + 4(l>>5) +
+// (i&3) for i = 0..15, so the head sum is 16 in-lane FMAs and one exchange
+// between the lane halves.
 template <int TQ>
-__global__ void __launch_bounds__(256) idx_decode_kernel(
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 1 ? 4 : 2))) idx_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const int32_t* __restrict__ vis_len, int T,
@@ -44,24 +62,21 @@ __global__ void __launch_bounds__(256) idx_decode_kernel(
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4;  // lane group: K slice of the operands, head quad of the result
-  const int n = lane & 15;
+  const int ln = lane & 31, hh = lane >> 5;
 
-  // A operands: the 32 heads of each query, two 16-head halves
-  v8i a0[TQ], a1[TQ];
-  float wq0[TQ][4], wq1[TQ][4];
+  v8i aq[TQ][2];
+  float wq[TQ][16];
   int vis[TQ];
 #pragma unroll
   for (int t = 0; t < TQ; ++t) {
     const int64_t bt = (int64_t)b * T + t0 + t;
-    const uint8_t* qrow = q8 + bt * (kIdxHeads * kIdxDim);
-    a0[t] = *(const v8i*)(qrow + n * kIdxDim + 32 * g);
-    a1[t] = *(const v8i*)(qrow + (16 + n) * kIdxDim + 32 * g);
+    const uint8_t* qrow = q8 + (bt * kIdxHeads + ln) * kIdxDim + 32 * hh;
+    aq[t][0] = *(const v8i*)(qrow);
+    aq[t][1] = *(const v8i*)(qrow + 64);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h0 = 4 * g + i, h1 = 16 + 4 * g + i;
-      wq0[t][i] = w[bt * kIdxHeads + h0] * q_scale[bt * kIdxHeads + h0];
-      wq1[t][i] = w[bt * kIdxHeads + h1] * q_scale[bt * kIdxHeads + h1];
+    for (int i = 0; i < 16; ++i) {
+      const int hd = 8 * (i >> 2) + 4 * hh + (i & 3);
+      wq[t][i] = w[bt * kIdxHeads + hd] * q_scale[bt * kIdxHeads + hd];
     }
     vis[t] = clamp_vis(vis_len[bt], L);
   }
@@ -73,46 +88,60 @@ __global__ void __launch_bounds__(256) idx_decode_kernel(
   int base = wg_begin + wave * kSuper;
   if (base >= wg_end) return;
 
-  auto load_tile = [&](int tile_base, v8i (&bv)[4]) {
+  // keys [tile_base + 32 blk + ln], K halves 0 and 1, and the scale of key
+  // tile_base + lane
+  auto load_tile = [&](int tile_base, v8i (&bv)[4], float& ks) {
+    const int sk = tile_base + lane;
+    ks = k_scale[key_base_b + (sk < L ? sk : L - 1)];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int key = tile_base + 16 * j + n;
+    for (int blk = 0; blk < 2; ++blk) {
+      int key = tile_base + 32 * blk + ln;
       key = key < L ? key : L - 1;
-      bv[j] = *(const v8i*)(k8 + (key_base_b + key) * kIdxDim + 32 * g);
+      const uint8_t* row = k8 + (key_base_b + key) * kIdxDim + 32 * hh;
+      bv[2 * blk] = *(const v8i*)(row);
+      bv[2 * blk + 1] = *(const v8i*)(row + 64);
     }
   };
 
-  v8i cur[4], nxt[4];
-  load_tile(base, cur);
-  for (; base < wg_end; base += kWaves * kSuper) {
-    const int next_base = base + kWaves * kSuper;
-    if (next_base < wg_end) load_tile(next_base, nxt);
-    const int my_key = base + lane;
-    const float ks = k_scale[key_base_b + (my_key < L ? my_key : L - 1)];
+  auto score_tile = [&](const v8i (&bv)[4], float ks, int tile_base) {
+    const int my_key = tile_base + lane;
 #pragma unroll
     for (int t = 0; t < TQ; ++t) {
-      float res = 0.f;
+      float r[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4f d0 = mfma_fp8_16x16x128(a0[t], cur[j]);
-        const v4f d1 = mfma_fp8_16x16x128(a1[t], cur[j]);
+      for (int blk = 0; blk < 2; ++blk) {
+        v16f d = mfma_fp8_32x32x64(aq[t][0], bv[2 * blk]);
+        d = mfma_fp8_32x32x64_acc(aq[t][1], bv[2 * blk + 1], d);
         float p = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p = fmaf(wq0[t][i], fmaxf(d0[i], 0.f), p);
-          p = fmaf(wq1[t][i], fmaxf(d1[i], 0.f), p);
-        }
-        p += __shfl_xor(p, 16, 64);
-        p += __shfl_xor(p, 32, 64);
-        res = (g == j) ? p : res;  // lane 16g+n keeps column tile g: key base + lane
+        for (int i = 0; i < 16; ++i) p = fmaf(wq[t][i], fmaxf(d[i], 0.f), p);
+        r[blk] = sum_halves(p);
       }
+      const float res = hh ? r[1] : r[0];  // lane l holds key tile_base + l
       if (my_key < wg_end) {
         const int64_t bt = (int64_t)b * T + t0 + t;
         scores[bt * L + my_key] = my_key < vis[t] ? res * ks : -INFINITY;
       }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+  };
+
+  // Two register buffers in turn, the next tile always in flight while the
+  // current one is scored. The prefetch is unconditional so that the wait
+  // before scoring only covers the older tile: past the end of the range it
+  // re-reads the tile being scored, which the caches hold.
+  constexpr int kStride = kWaves * kSuper;
+  v8i ta[4], tb[4];
+  float ka, kb;
+  load_tile(base, ta, ka);
+  for (;;) {
+    load_tile(base + kStride < wg_end ? base + kStride : base, tb, kb);
+    score_tile(ta, ka, base);
+    base += kStride;
+    if (base >= wg_end) break;
+    load_tile(base + kStride < wg_end ? base + kStride : base, ta, ka);
+    score_tile(tb, kb, base);
+    base += kStride;
+    if (base >= wg_end) break;
   }
 }
 
