@@ -68,6 +68,20 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return (uint16_t)(a >> 16);
 }
 
+// Workgroup barrier for data exchanged through LDS only. A workgroup fence
+// would also wait for every outstanding global store and global->LDS load of
+// the wave (vmcnt(0)), which a pipeline keeps in flight on purpose; instead
+// each wave waits for its own LDS accesses (lgkmcnt), and the empty asm
+// statements keep the compiler from moving memory accesses across s_barrier.
+// Global->LDS loads must be waited for (vmcnt) by the issuing wave before it
+// reaches the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---- launchers (host) ----
 
 hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float* w,

@@ -20,6 +20,9 @@ namespace {
 #ifndef LCS_IDX_TARGET_WGS
 #define LCS_IDX_TARGET_WGS 1024
 #endif
+#ifndef LCS_IDX_PREFILL_MIN_T
+#define LCS_IDX_PREFILL_MIN_T 16
+#endif
 #ifndef LCS_IDX_MAX_ITERS
 #define LCS_IDX_MAX_ITERS 16
 #endif
@@ -145,11 +148,180 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
   }
 }
 
+// Prefill (many queries per sequence): a dense FP8 contraction of the query
+// heads [T*32 x 128] with the keys [128 x L], each product passed through the
+// ReLU-weighted head sum. Eight waves per workgroup; each wave keeps 128 keys
+// (four 32-key MFMA column blocks, both K halves) in registers for the whole
+// launch, so the workgroup covers 1024 keys, and the workgroup's queries
+// stream through LDS in chunks of 8 (32 KB of codes + the 8 x 32 combined head
+// weights w * q_scale), double-buffered: the global loads of chunk c+1 are in
+// registers while chunk c is scored, and are written to LDS before the one
+// barrier per chunk. Query rows sit in LDS with their 16-byte granules
+// XOR-swizzled by (row & 7), so the MFMA operand reads are free of bank
+// conflicts. Per (query, 32 keys): two MFMAs (8192 MACs per pair) and, per
+// lane, 16 max + 16 FMA for its 16 heads plus one lane-half exchange.
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = kPfWaves * 64;
+constexpr int kPfKeysPerWave = 128;
+constexpr int kPfKeysPerWg = kPfWaves * kPfKeysPerWave;  // 1024
+constexpr int kPfChunk = 8;                              // queries per LDS chunk
+constexpr int kPfQBytes = kPfChunk * kIdxHeads * kIdxDim;  // 32768
+constexpr int kPfWBytes = kPfChunk * kIdxHeads * 4;        // 1024
+constexpr int kPfBufBytes = kPfQBytes + kPfWBytes;
+
+__global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
+    const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k8,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ vis_len, int T, int L,
+    int queries_per_wg, float* __restrict__ scores) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[2][kPfBufBytes];
+
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ln = lane & 31, hh = lane >> 5;
+  const int t_begin = blockIdx.y * queries_per_wg;
+  const int t_end = min(T, t_begin + queries_per_wg);
+  if (t_begin >= t_end) return;
+
+  const int64_t key_base_b = (int64_t)b * L;
+  const int kw0 = blockIdx.x * kPfKeysPerWg + wave * kPfKeysPerWave;
+
+  // this wave's keys: block kb holds keys kw0 + 32 kb + (lane & 31)
+  v8i kreg[4][2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    int key = kw0 + 32 * kb + ln;
+    key = key < L ? key : L - 1;
+    const uint8_t* row = k8 + (key_base_b + key) * kIdxDim + 32 * hh;
+    kreg[kb][0] = *(const v8i*)(row);
+    kreg[kb][1] = *(const v8i*)(row + 64);
+  }
+  // scales of the keys this lane stores: kw0 + 64 c + lane
+  float ks[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int key = kw0 + 64 * c + lane;
+    ks[c] = k_scale[key_base_b + (key < L ? key : L - 1)];
+  }
+
+  // chunk loads: thread tid carries granules tid + 512 r (r < 4) of the
+  // chunk's 2048 16-byte query granules, and (tid < 256) one combined weight
+  v4i gq[4];
+  float gw = 0.f;
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = tid + kPfThreads * r;
+      int t = c0 + (g >> 8);
+      t = t < T ? t : T - 1;
+      gq[r] = *(const v4i*)(q8 + (((int64_t)b * T + t) * kIdxHeads * kIdxDim) + 16 * (g & 255));
+    }
+    if (tid < kPfChunk * kIdxHeads) {
+      int t = c0 + (tid >> 5);
+      t = t < T ? t : T - 1;
+      const int i = tid & 15, h2 = (tid >> 4) & 1;
+      const int head = 8 * (i >> 2) + 4 * h2 + (i & 3);
+      const int64_t o = ((int64_t)b * T + t) * kIdxHeads + head;
+      gw = w[o] * q_scale[o];
+    }
+  };
+  auto store_chunk = [&](uint8_t* buf) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = tid + kPfThreads * r;
+      const int row = g >> 3, c = g & 7;  // row = query * 32 + head
+      *(v4i*)(buf + row * kIdxDim + 16 * (c ^ (row & 7))) = gq[r];
+    }
+    // weights as [query][lane half][16]: the 16 heads a lane half holds
+    if (tid < kPfChunk * kIdxHeads) ((float*)(buf + kPfQBytes))[tid] = gw;
+  };
+
+  auto score_chunk = [&](const uint8_t* buf, int c0) {
+    const int nq = min(kPfChunk, t_end - c0);
+    for (int qi = 0; qi < nq; ++qi) {
+      const int t = c0 + qi;
+      const int64_t bt = (int64_t)b * T + t;
+      const uint8_t* qrow = buf + qi * (kIdxHeads * kIdxDim) + ln * kIdxDim;
+      const int sw = ln & 7;
+      v8i a[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int c = 2 * hh + 4 * kh;
+        const v4i lo = *(const v4i*)(qrow + 16 * (c ^ sw));
+        const v4i hi = *(const v4i*)(qrow + 16 * ((c + 1) ^ sw));
+        a[kh] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      const float* wrow = (const float*)(buf + kPfQBytes) + qi * kIdxHeads + 16 * hh;
+      float wq[16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const v4f v = *(const v4f*)(wrow + 4 * m);
+        wq[4 * m] = v[0];
+        wq[4 * m + 1] = v[1];
+        wq[4 * m + 2] = v[2];
+        wq[4 * m + 3] = v[3];
+      }
+      const int vis = clamp_vis(vis_len[bt], L);
+      float r[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        v16f d = mfma_fp8_32x32x64(a[0], kreg[kb][0]);
+        d = mfma_fp8_32x32x64_acc(a[1], kreg[kb][1], d);
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p = fmaf(wq[i], fmaxf(d[i], 0.f), p);
+        r[kb] = sum_halves(p);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float res = hh ? r[2 * c + 1] : r[2 * c];  // lane l: key kw0 + 64 c + l
+        const int key = kw0 + 64 * c + lane;
+        if (key < L) scores[bt * L + key] = key < vis ? res * ks[c] : -INFINITY;
+      }
+    }
+  };
+
+  load_chunk(t_begin);
+  store_chunk(s_buf[0]);
+  lds_barrier();
+  for (int c0 = t_begin;;) {
+    const int c1 = c0 + kPfChunk;
+    if (c1 < t_end) load_chunk(c1);
+    score_chunk(s_buf[0], c0);
+    if (c1 >= t_end) break;
+    store_chunk(s_buf[1]);
+    lds_barrier();
+    c0 = c1;
+    const int c2 = c0 + kPfChunk;
+    if (c2 < t_end) load_chunk(c2);
+    score_chunk(s_buf[1], c0);
+    if (c2 >= t_end) break;
+    store_chunk(s_buf[0]);
+    lds_barrier();
+    c0 = c2;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
                             const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
                             int B, int T, int L, float* scores, hipStream_t stream) {
+  if (T >= LCS_IDX_PREFILL_MIN_T) {
+    // workgroups: key blocks of 1024 x query ranges x batch, the query ranges
+    // (multiples of the 8-query chunk) sized for about 4 workgroups per CU
+    const int gx = (L + kPfKeysPerWg - 1) / kPfKeysPerWg;
+    const int chunks = (T + kPfChunk - 1) / kPfChunk;
+    int64_t want = (1024 + (int64_t)gx * B - 1) / ((int64_t)gx * B);
+    if (want < 1) want = 1;
+    if (want > chunks) want = chunks;
+    const int per = (int)((chunks + want - 1) / want) * kPfChunk;
+    const int gy = (T + per - 1) / per;
+    return launch_kernel(idx_prefill_kernel, dim3(gx, gy, B), dim3(kPfThreads), 0, stream, q8,
+                         q_scale, w, k8, k_scale, vis_len, T, L, per, scores);
+  }
   // keys per workgroup: a multiple of 4 waves x 64 keys, sized for enough WGs
   const int64_t total_keys = (int64_t)B * L;
   int64_t iters = total_keys / ((int64_t)LCS_IDX_TARGET_WGS * kWaves * kSuper);

@@ -116,18 +116,6 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
   }
 }
 
-// Workgroup barrier for the tile pipeline. A workgroup fence would drain every
-// in-flight global->LDS load (they count as LDS writes), including those of
-// later tiles, so instead: each wave has already waited for its own loads of
-// the tile (vmcnt), waits here for its LDS writes (lgkmcnt), and the empty asm
-// statements keep the compiler from moving memory accesses across s_barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Per-workgroup state of the attention loop. Eight waves: wave w serves head
 // group hg = w & 1 (32 heads) and dim quarter dq = w >> 1. It computes the
 // partial S over dims [144 dq, 144 dq + 144) and the output dims

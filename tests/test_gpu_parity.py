@@ -49,8 +49,11 @@ def test_device_generator_matches_host():
 
 
 # ------------------------------------------------------------------ indexer
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 16, 24, 37])
 def test_idx_score_matches_oracle(T):
+    """T < 16: the key-streaming kernel (T > 4 in chunks of 4); T >= 16: the
+    tiled prefill kernel (8-query chunks, 1024-key blocks; L = 8229 leaves a
+    ragged last block and T = 37 a ragged last chunk)."""
     _say("case: idx_score T=%d" % T)
     B, L = 2, 8192 + 37
     w = wl.Workload("idx-parity", seed=40 + T, B=B, T=T, L=L, n_layers=1, plant_permyriad=100)
@@ -67,6 +70,28 @@ def test_idx_score_matches_oracle(T):
                   to_dev(inp["k_scale"]), to_dev(vis), scores)
     rel = check_scores(scores.cpu().numpy(), ref64)
     _say("  max rel err %.3g" % rel)
+
+
+def test_idx_score_prefill_full_size_sampled():
+    """The chunked-prefill shape (4096 causal queries at the end of a 131072
+    position cache), in the launch configuration the benchmark uses; rows
+    sampled across the chunks and query ranges checked against the oracle."""
+    w = wl.WORKLOADS["prefill"]
+    _say("case: idx_score prefill full size %s" % w.name)
+    B, T, L = w.B, w.T, w.L
+    d = wl.dev_indexer(w, 0, DEV)
+    vis = w.vis_len()
+    scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+    lcs.idx_score(d["q8"], d["q_scale"], d["w"], d["k8"], d["k_scale"], to_dev(vis), scores)
+    torch.cuda.synchronize()
+    del d
+    inp = wl.host_indexer(w, 0)
+    for t in (0, 7, 8, 1023, 2050, 4095):
+        _, ref64 = oracle.idx_score(inp["q8"][:, t:t + 1], inp["q_scale"][:, t:t + 1],
+                                    inp["w"][:, t:t + 1], inp["k8"], inp["k_scale"],
+                                    vis[:, t:t + 1], want64=True)
+        rel = check_scores(scores[:, t:t + 1].cpu().numpy(), ref64, "row t=%d" % t)
+        _say("  t=%d max rel err %.3g" % (t, rel))
 
 
 # ------------------------------------------------------------------ top-k
