@@ -68,6 +68,13 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return (uint16_t)(a >> 16);
 }
 
+// s_waitcnt vmcnt(N) with the other counters left unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroup barrier for data exchanged through LDS only. A workgroup fence
 // would also wait for every outstanding global store and global->LDS load of
 // the wave (vmcnt(0)), which a pipeline keeps in flight on purpose; instead

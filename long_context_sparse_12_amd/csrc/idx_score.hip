@@ -43,9 +43,25 @@ __device__ __forceinline__ v16f mfma_fp8_32x32x64_acc(const v8i& a, const v8i& b
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// max(x, 0) as one v_med3_f32. fmaxf would add a canonicalising max on the
+// MFMA result (NaN quieting), i.e. two VALU ops per element instead of one.
+// The dot products are bounded by 128 * 448^2, so the median of (x, 0, 3e38)
+// is max(x, 0) (an infinite bound would be folded back into a max).
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.0e38f); }
+
 // sum of a value across the two 32-lane halves (lane l and l^32), VALU only
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// For two per-lane partial sums x, y over the lane halves' heads: lanes
+// 0..31 get x(l) + x(l + 32), lanes 32..63 get y(l - 32) + y(l), i.e. the
+// full head sums of block x in the low half and of block y in the high half,
+// with one v_permlane32_swap (it swaps the high half of x with the low half
+// of y) and one add.
+__device__ __forceinline__ float sum_pair(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
@@ -117,7 +133,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
         d = mfma_fp8_32x32x64_acc(aq[t][1], bv[2 * blk + 1], d);
         float p = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) p = fmaf(wq[t][i], fmaxf(d[i], 0.f), p);
+        for (int i = 0; i < 16; ++i) p = fmaf(wq[t][i], relu(d[i]), p);
         r[blk] = sum_halves(p);
       }
       const float res = hh ? r[1] : r[0];  // lane l holds key tile_base + l
@@ -156,18 +172,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
 // stream through LDS in chunks of 8 (32 KB of codes + the 8 x 32 combined head
 // weights w * q_scale), double-buffered: the global loads of chunk c+1 are in
 // registers while chunk c is scored, and are written to LDS before the one
-// barrier per chunk. Query rows sit in LDS with their 16-byte granules
-// XOR-swizzled by (row & 7), so the MFMA operand reads are free of bank
+// barrier per chunk. Query rows (128 B) sit in LDS with their 16-byte
+// granules XOR-swizzled by (row >> 1) & 7: 16 lanes reading 16 consecutive
+// rows then cover all 64 banks, so the MFMA operand reads are free of bank
 // conflicts. Per (query, 32 keys): two MFMAs (8192 MACs per pair) and, per
 // lane, 16 max + 16 FMA for its 16 heads plus one lane-half exchange.
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * 64;
-constexpr int kPfKeysPerWave = 128;
-constexpr int kPfKeysPerWg = kPfWaves * kPfKeysPerWave;  // 1024
+#ifndef LCS_PF_KB
+#define LCS_PF_KB 4
+#endif
+constexpr int kPfKB = LCS_PF_KB;  // 32-key MFMA column blocks per wave
+constexpr int kPfKeysPerWave = 32 * kPfKB;
+constexpr int kPfKeysPerWg = kPfWaves * kPfKeysPerWave;
 constexpr int kPfChunk = 8;                              // queries per LDS chunk
 constexpr int kPfQBytes = kPfChunk * kIdxHeads * kIdxDim;  // 32768
 constexpr int kPfWBytes = kPfChunk * kIdxHeads * 4;        // 1024
 constexpr int kPfBufBytes = kPfQBytes + kPfWBytes;
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 (gfx9): 32-bit data format
 
 __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
@@ -189,9 +211,9 @@ __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
   const int kw0 = blockIdx.x * kPfKeysPerWg + wave * kPfKeysPerWave;
 
   // this wave's keys: block kb holds keys kw0 + 32 kb + (lane & 31)
-  v8i kreg[4][2];
+  v8i kreg[kPfKB][2];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < kPfKB; ++kb) {
     int key = kw0 + 32 * kb + ln;
     key = key < L ? key : L - 1;
     const uint8_t* row = k8 + (key_base_b + key) * kIdxDim + 32 * hh;
@@ -199,18 +221,28 @@ __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
     kreg[kb][1] = *(const v8i*)(row + 64);
   }
   // scales of the keys this lane stores: kw0 + 64 c + lane
-  float ks[2];
+  float ks[kPfKB / 2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < kPfKB / 2; ++c) {
     const int key = kw0 + 64 * c + lane;
     ks[c] = k_scale[key_base_b + (key < L ? key : L - 1)];
   }
+  // Wait for the keys here: left pending, the compiler would wait with
+  // vmcnt(0) at their first use inside the chunk loop, which also waits for
+  // the next chunk's loads in flight.
+  wait_vm<0>();
 
   // chunk loads: thread tid carries granules tid + 512 r (r < 4) of the
   // chunk's 2048 16-byte query granules, and (tid < 256) one combined weight
   v4i gq[4];
-  float gw = 0.f;
+  float gw = 0.f, gs = 0.f;
+  int gv = 0, vis_cur = 0;  // lanes 0..7: visible lengths of the chunk's queries
   auto load_chunk = [&](int c0) {
+    {
+      int t = c0 + (lane & 7);
+      t = t < T ? t : T - 1;
+      gv = vis_len[(int64_t)b * T + t];
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int g = tid + kPfThreads * r;
@@ -224,7 +256,8 @@ __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
       const int i = tid & 15, h2 = (tid >> 4) & 1;
       const int head = 8 * (i >> 2) + 4 * h2 + (i & 3);
       const int64_t o = ((int64_t)b * T + t) * kIdxHeads + head;
-      gw = w[o] * q_scale[o];
+      gw = w[o];
+      gs = q_scale[o];
     }
   };
   auto store_chunk = [&](uint8_t* buf) {
@@ -232,54 +265,83 @@ __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
     for (int r = 0; r < 4; ++r) {
       const int g = tid + kPfThreads * r;
       const int row = g >> 3, c = g & 7;  // row = query * 32 + head
-      *(v4i*)(buf + row * kIdxDim + 16 * (c ^ (row & 7))) = gq[r];
+      *(v4i*)(buf + row * kIdxDim + 16 * (c ^ ((row >> 1) & 7))) = gq[r];
     }
     // weights as [query][lane half][16]: the 16 heads a lane half holds
-    if (tid < kPfChunk * kIdxHeads) ((float*)(buf + kPfQBytes))[tid] = gw;
+    if (tid < kPfChunk * kIdxHeads) ((float*)(buf + kPfQBytes))[tid] = gw * gs;
+    vis_cur = gv;
+  };
+
+  // All 8 queries of a chunk are scored, with the same instruction stream
+  // whatever the query or key range: a query past the range or a key past L
+  // is dropped by the buffer store's range check. So each chunk issues a
+  // fixed number of stores and the waits for the next chunk's loads never
+  // have to cover them.
+  //
+  // The 32 (query, key block) units of a chunk run as a software pipeline:
+  // unit u issues the two MFMAs of unit u + 2 and then the epilogue of unit
+  // u, whose MFMAs have finished by then, so the epilogue never waits on the
+  // matrix core. Query qi + 1's operands are read from LDS at qi's first unit.
+  // A scheduling barrier after each unit keeps this order.
+  auto lds_query = [&](const uint8_t* buf, int qi, v8i (&a)[2], float (&wq)[16]) {
+    const uint8_t* qrow = buf + qi * (kIdxHeads * kIdxDim) + ln * kIdxDim;
+    const int sw = (ln >> 1) & 7;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int c = 2 * hh + 4 * kh;
+      const v4i lo = *(const v4i*)(qrow + 16 * (c ^ sw));
+      const v4i hi = *(const v4i*)(qrow + 16 * ((c + 1) ^ sw));
+      a[kh] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    const float* wrow = (const float*)(buf + kPfQBytes) + qi * kIdxHeads + 16 * hh;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const v4f v = *(const v4f*)(wrow + 4 * m);
+      wq[4 * m] = v[0];
+      wq[4 * m + 1] = v[1];
+      wq[4 * m + 2] = v[2];
+      wq[4 * m + 3] = v[3];
+    }
   };
 
   auto score_chunk = [&](const uint8_t* buf, int c0) {
-    const int nq = min(kPfChunk, t_end - c0);
-    for (int qi = 0; qi < nq; ++qi) {
-      const int t = c0 + qi;
-      const int64_t bt = (int64_t)b * T + t;
-      const uint8_t* qrow = buf + qi * (kIdxHeads * kIdxDim) + ln * kIdxDim;
-      const int sw = ln & 7;
-      v8i a[2];
+    v8i A[2][2];
+    float W[2][16];
+    v16f D[3];
+    float P[2];
+    lds_query(buf, 0, A[0], W[0]);
+    auto mma = [&](int u) {
+      const int qi = u / kPfKB, kb = u % kPfKB;
+      D[u % 3] = mfma_fp8_32x32x64(A[qi & 1][0], kreg[kb][0]);
+      D[u % 3] = mfma_fp8_32x32x64_acc(A[qi & 1][1], kreg[kb][1], D[u % 3]);
+    };
+    mma(0);
+    mma(1);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int kUnits = kPfKB * kPfChunk;
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const int c = 2 * hh + 4 * kh;
-        const v4i lo = *(const v4i*)(qrow + 16 * (c ^ sw));
-        const v4i hi = *(const v4i*)(qrow + 16 * ((c + 1) ^ sw));
-        a[kh] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-      const float* wrow = (const float*)(buf + kPfQBytes) + qi * kIdxHeads + 16 * hh;
-      float wq[16];
+    for (int u = 0; u < kUnits; ++u) {
+      const int qi = u / kPfKB, kb = u % kPfKB;
+      if (kb == 0 && qi + 1 < kPfChunk) lds_query(buf, qi + 1, A[(qi + 1) & 1], W[(qi + 1) & 1]);
+      if (u + 2 < kUnits) mma(u + 2);
+      float acc = 0.f;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const v4f v = *(const v4f*)(wrow + 4 * m);
-        wq[4 * m] = v[0];
-        wq[4 * m + 1] = v[1];
-        wq[4 * m + 2] = v[2];
-        wq[4 * m + 3] = v[3];
-      }
-      const int vis = clamp_vis(vis_len[bt], L);
-      float r[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        v16f d = mfma_fp8_32x32x64(a[0], kreg[kb][0]);
-        d = mfma_fp8_32x32x64_acc(a[1], kreg[kb][1], d);
-        float p = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p = fmaf(wq[i], fmaxf(d[i], 0.f), p);
-        r[kb] = sum_halves(p);
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float res = hh ? r[2 * c + 1] : r[2 * c];  // lane l: key kw0 + 64 c + l
+      for (int i = 0; i < 16; ++i) acc = fmaf(W[qi & 1][i], relu(D[u % 3][i]), acc);
+      P[kb & 1] = acc;
+      if (kb & 1) {
+        const int c = kb >> 1;
+        const int t = c0 + qi;
+        const int64_t bt = (int64_t)b * T + (t < t_end ? t : t_end - 1);
+        const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+            scores + bt * L, 0, t < t_end ? L * 4 : 0, kBufferWord3);
+        const int vis = clamp_vis(__builtin_amdgcn_readlane(vis_cur, qi), L);
+        // lane l: key kw0 + 64 c + l (blocks 2c and 2c+1 by lane half)
+        const float res = sum_pair(P[0], P[1]) * ks[c];
         const int key = kw0 + 64 * c + lane;
-        if (key < L) scores[bt * L + key] = key < vis ? res * ks[c] : -INFINITY;
+        const float v = key < vis ? res : -INFINITY;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out, 4 * key, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 

@@ -98,13 +98,6 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint8_t* lds_base) {
                                    (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
 }
 
-// s_waitcnt vmcnt(N) with the other counters left unconstrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // wait until at most `ahead` tiles of `per` loads each are still in flight
 template <int PER>
 __device__ __forceinline__ void wait_tiles(int ahead) {
