@@ -25,6 +25,7 @@ if ROOT not in sys.path:
 
 METRIC = ("decode tokens/s/GPU at L=128K & 1M (indexer+top-k+sparse attn); % HBM roofline")
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
 IDX_BYTES_PER_KEY = 132  # 128 E4M3 codes + fp32 scale
 IDX_BYTES_PER_QUERY = 32 * 128 + 32 * 4 + 32 * 4  # q8, q_scale, w
 ATT_BYTES_PER_QUERY_IO = 64 * 576 * 2 + 64 * 512 * 2 + 64 * 4  # q, out, lse
@@ -33,7 +34,9 @@ ROTATIONS = 3  # query sets cycled between steps so no step reuses another's gat
 # HBM traffic of the indexer launch from rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
 # scaled by the copy-kernel calibration; valid only for the kernel source it was
 # taken on (sha256 of csrc/idx_score.hip, first 16 hex digits).
-TRAFFIC = {}
+TRAFFIC = {
+    "decode-B32-L131072-group4": {"sha": "f1d1c6bc9763228a", "bytes": 572301099},
+}
 
 
 def _sha(path):
@@ -47,13 +50,16 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode128k",
-                    choices=["tiny", "decode128k", "decode1m", "mtp1m"])
+                    choices=["tiny", "decode128k", "prefill", "decode1m", "mtp1m"])
     ap.add_argument("--cpu-rows", type=int, default=None, help="sequences in the oracle sample")
     ap.add_argument("--cpu-layers", type=int, default=None, help="layers in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-off", action="store_true", help="skip the IndexShare-off run")
     ap.add_argument("--only-composite", action="store_true",
                     help="time the composite steps only (for profiling runs)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (3 times), the "
+                         "reference kernel for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -255,6 +261,14 @@ def main():
     from synth import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     has_off = (w.n_layers > 1) and not args.no_off
     t_setup = time.time()
     s = Setup(w, want_off=has_off)
@@ -267,7 +281,7 @@ def main():
     sb = step_bytes(w, False)
     res = {
         "metric": METRIC, "value": round(value, 1),
-        "unit": "draft tokens/s" if w.mtp_steps else "tokens/s",
+        "unit": "draft tokens/s" if w.mtp_steps else ("prefill tokens/s" if w.T > 4 else "tokens/s"),
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8+bf16 (fp32 accumulate)", "data": "synthetic",
@@ -281,15 +295,27 @@ def main():
     if not args.only_composite:
         ker, counts = kernel_breakdown(s, lcs, max(args.steps // 2, 3))
         idx_us = ker["idx_score"]
-        launch_bytes = w.B * w.L * IDX_BYTES_PER_KEY + w.B * w.T * IDX_BYTES_PER_QUERY
-        achieved = launch_bytes / (idx_us * 1e-6) / 1e9
         sha = _sha(os.path.join(ROOT, "long_context_sparse_12_amd", "csrc", "idx_score.hip"))
         tr = TRAFFIC.get(w.name)
         traffic = tr["bytes"] if tr and tr["sha"] == sha else None
-        res["roofline"] = {"kernel": "idx_score (decode indexer)", "bound": "hbm",
-                           "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                           "bytes_per_launch": launch_bytes, "avg_launch_us": round(idx_us, 2)}
+        if w.T > 4:
+            # dense FP8 contraction: 32 heads x 128 dims = 4096 MACs = 8192 FLOP per
+            # visible (t, s) pair
+            flops = 8192.0 * float(w.vis_len().astype("int64").sum())
+            achieved = flops / (idx_us * 1e-6) / 1e12
+            res["roofline"] = {"kernel": "idx_score (prefill indexer)", "bound": "mfma",
+                               "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                               "traffic": traffic, "flop_per_launch": flops,
+                               "avg_launch_us": round(idx_us, 2)}
+        else:
+            launch_bytes = w.B * w.L * IDX_BYTES_PER_KEY + w.B * w.T * IDX_BYTES_PER_QUERY
+            achieved = launch_bytes / (idx_us * 1e-6) / 1e9
+            res["roofline"] = {"kernel": "idx_score (decode indexer)", "bound": "hbm",
+                               "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                               "traffic": traffic, "bytes_per_launch": launch_bytes,
+                               "avg_launch_us": round(idx_us, 2)}
         res["kernels_us"] = {k: round(v, 2) for k, v in ker.items()}
         res["launches_per_step"] = {k: v // max(args.steps // 2, 3) for k, v in counts.items()}
     if has_off:
