@@ -54,18 +54,15 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 
 __device__ __forceinline__ int clamp_vis(int v, int L) { return v < 0 ? 0 : (v > L ? L : v); }
 
-// two fp32 -> packed bf16 pair, round to nearest even
+// two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-  a += 0x7FFFu + ((a >> 16) & 1u);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (a >> 16) | (b & 0xFFFF0000u);
+  const v2bf r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t a = __float_as_uint(f);
-  a += 0x7FFFu + ((a >> 16) & 1u);
-  return (uint16_t)(a >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // s_waitcnt vmcnt(N) with the other counters left unconstrained (gfx9 encoding)

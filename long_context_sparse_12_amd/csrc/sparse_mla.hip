@@ -431,54 +431,495 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 latent KV: split roles. The 64 x 32 logits of a 32-row tile need K =
+// 576 per output element, so splitting the dims over waves (as above) costs
+// an exchange of partial logits per tile. Here two "S waves" (one per head
+// group of 32) each hold their group's whole Q^T (36 K-steps, 144 VGPRs) and
+// compute the full S^T[32 rows x 32 heads] of a tile alone, then the online
+// softmax, and hand P^T (bf16, 2 KB per head group) and the rescale factor to
+// four "PV waves" through LDS. PV wave (hg, dh) owns O^T for 256 output dims
+// of its head group (8 accumulators, 128 VGPRs). Two "gather waves" issue the
+// row gathers. Waves land on SIMD (wave & 3): the S waves (0, 1) share their
+// SIMDs only with the gather waves (4, 5), which use no MFMA, and the PV waves
+// (2, 3, 6, 7) fill SIMDs 2 and 3, so each SIMD's matrix core gets 36 (S) or
+// 2 x 16 (PV) MFMAs per tile. The roles work on consecutive tiles at the same
+// time (S waves on tile j+1 while PV waves finish tile j), with one barrier
+// per tile; four stage buffers give every gather two tiles of lead time.
+constexpr int kWavesB = 8;
+constexpr int kThreadsB = 64 * kWavesB;
+constexpr int kStagesB = 4;
+constexpr int kMaxSplitRowsB = 512;
+constexpr int kGatherWaves = 2;
+constexpr int kDmaPerB = kTileBytes / 1024 / kGatherWaves;  // 18 gathers per lane per tile
+
+enum Role { kRoleS, kRolePV, kRoleGather };
+__device__ __forceinline__ Role role_of(int wave) {
+  return wave < 2 ? kRoleS : (wave == 4 || wave == 5) ? kRoleGather : kRolePV;
+}
+
+#ifndef LCS_ATTN_S_AHEAD
+#define LCS_ATTN_S_AHEAD 8
+#endif
+#ifndef LCS_ATTN_B_TARGET_WGS
+#define LCS_ATTN_B_TARGET_WGS 256
+#endif
+#ifndef LCS_ATTN_B_MAX_SPLITS
+#define LCS_ATTN_B_MAX_SPLITS 64
+#endif
+
+__host__ __device__ inline SplitPlan plan_splits_b(int64_t queries, int k) {
+  SplitPlan p;
+  int64_t s = (LCS_ATTN_B_TARGET_WGS + queries - 1) / queries;
+  const int64_t min_s = (k + kMaxSplitRowsB - 1) / kMaxSplitRowsB;
+  const int64_t max_s = (k + kTileRows - 1) / kTileRows;
+  if (s > max_s) s = max_s;
+  if (s > LCS_ATTN_B_MAX_SPLITS) s = LCS_ATTN_B_MAX_SPLITS;
+  if (s < min_s) s = min_s;
+  if (s < 1) s = 1;
+  int64_t r = (k + s - 1) / s;
+  r = (r + kTileRows - 1) / kTileRows * kTileRows;
+  p.rows_per_split = (int)r;
+  p.splits = (int)((k + r - 1) / r);
+  return p;
+}
+
+// LDS layout of a bf16 tile in this kernel: granule c of row r sits at
+// (c & ~7) | ((c & 7) ^ swz_b(r)) with swz_b(r) = 4 * bit1(r) + bits 3..2 (r).
+// The LDS serves 256 bytes per cycle: 16 lanes of a 16-byte read or 32 lanes
+// of an 8-byte one. For the S operand (16 lanes = rows 0..15 or 16..31 at one
+// granule) swz_b is a bijection on the even and on the odd rows; for the
+// transposing V reads (32 lanes = 4 rows x 4 granules of an aligned group)
+// rows r and r + 2 differ in bit 2 of the swizzle. Both are then free of bank
+// conflicts (row 8 apart: swz_b(r + 8) = swz_b(r) ^ 2; 16 apart: equal).
+__device__ __forceinline__ int swz_b(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+// state shared by both roles
+struct AttnB {
+  uint8_t* st[kStagesB];
+  uint8_t* p_buf;   // [2 parity][2 hg][64 lanes][32 B]  P^T B operands
+  float* alpha;     // [2 parity][2 hg][32 heads]
+  int* flag;        // [2 parity][2 hg]
+  const int32_t* s_idx;
+  int n_tiles;
+  int wave, lane, hg;
+};
+
+struct SWave {
+  v8bf qT[36];  // Q^T: head 32hg + (lane&31), dims 16ks + 8(lane>>5) .. +8
+  float c_log;
+  float m_run, l_run;
+};
+
+struct PWave {
+  v16f acc[8];  // O^T: dims 256dh + 32mt + (row of the 32x32 tile), heads as columns
+  int dh;
+};
+
+struct GWave {
+  int g;  // 0 or 1
+  const uint8_t* kv8;
+  int64_t kv_b;
+  int dma_row[kDmaPerB];  // row inside the tile of each gather
+  int dma_off[kDmaPerB];  // byte offset inside the row (swizzled granule)
+};
+
+// gathers of `tile` into stage S: gather-wave lane (g, l), gather i covers
+// LDS bytes [1024 (g + 2 i), +1024) of the stage, 16 bytes per lane
+template <int S>
+__device__ __forceinline__ void issue_tile_b(const AttnB& c, const GWave& w, int tile) {
+  int32_t rows[kDmaPerB];
+#pragma unroll
+  for (int i = 0; i < kDmaPerB; ++i) rows[i] = c.s_idx[tile * kTileRows + w.dma_row[i]];
+#pragma unroll
+  for (int i = 0; i < kDmaPerB; ++i) {
+    const int32_t s = rows[i] >= 0 ? rows[i] : 0;  // padding rows load row 0 (masked)
+    dma16(w.kv8 + (w.kv_b + s) * (int64_t)kRowBytes + w.dma_off[i],
+          c.st[S] + 1024 * (w.g + kGatherWaves * i));
+  }
+}
+
+// S^T of one tile and its softmax (S waves); P^T, alpha and the rescale flag
+// go to parity buffer `par`
+template <int S>
+__device__ __forceinline__ void s_phase(const AttnB& c, SWave& w, int tile, int par) {
+  const int lane = c.lane, ln = lane & 31, h = lane >> 5;
+  const uint8_t* tb = c.st[S];
+  const uint8_t* sb[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) sb[m] = tb + ln * kRowBytes + 16 * ((2 * m + h) ^ swz_b(ln));
+  // A operand of K-step ks: lane holds row (lane&31), dims 16ks + 8h .. +8
+  // (granule 2ks + h). The reads run LCS_ATTN_S_AHEAD K-steps ahead of the
+  // MFMAs, so the LDS latency is paid once per tile, not once per K-step.
+  constexpr int kAhead = LCS_ATTN_S_AHEAD;
+  v4i a[kAhead];
+#pragma unroll
+  for (int ks = 0; ks < kAhead; ++ks) a[ks] = *(const v4i*)(sb[ks & 3] + 128 * (ks >> 2));
+  v16f se, so;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { se[i] = 0.f; so[i] = 0.f; }
+  // scheduling barriers keep each read kAhead K-steps before its MFMA (the
+  // scheduler would otherwise sink the reads next to their uses)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < 36; ks += 2) {
+    se = mfma32_bf16(as_v8bf(a[ks % kAhead]), w.qT[ks], se);
+    so = mfma32_bf16(as_v8bf(a[(ks + 1) % kAhead]), w.qT[ks + 1], so);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int nk = ks + e + kAhead;
+      if (nk < 36) a[(ks + e) % kAhead] = *(const v4i*)(sb[nk & 3] + 128 * (nk >> 2));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // validity of the tile's rows as a wave-uniform bit mask (bit r: row r has
+  // a position); a tile without padding skips the masking
+  const uint32_t valid = (uint32_t)__ballot(c.s_idx[tile * kTileRows + ln] >= 0);
+  // lane holds head 32hg + (lane&31) for rows 8(i/4) + 4h + (i&3)
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = (se[i] + so[i]) * w.c_log;
+  if (valid != 0xFFFFFFFFu) {
+    const uint32_t mine = valid >> (4 * h);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!((mine >> (8 * (i >> 2) + (i & 3))) & 1u)) t[i] = -INFINITY;
+  }
+  float mx = t[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, t[i]);
+  {
+    // the other lane half holds the same head's other 16 rows
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  // lazy rescaling, as in the split-dims kernel above
+  const bool first = w.m_run == -INFINITY;
+  const float m_new = (first || mx > w.m_run + kRescaleSlack) ? mx : w.m_run;
+  float p[16];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p[i] = (t[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(t[i] - m_new);
+    psum += p[i];
+  }
+  const bool rescale = __ballot(!first && m_new != w.m_run) != 0;
+  if (rescale) {
+    const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(w.m_run - m_new);
+    w.l_run *= alpha;
+    if (h == 0) c.alpha[(par * 2 + c.hg) * 32 + ln] = alpha;
+  }
+  w.l_run += psum;
+  w.m_run = m_new;
+  if (lane == 0) c.flag[par * 2 + c.hg] = rescale ? 1 : 0;
+  uint8_t* pb = c.p_buf + ((par * 2 + c.hg) * 64 + lane) * 32;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int o = 8 * ks;
+    *(v4i*)(pb + 16 * ks) = v4i{(int)pack_bf16x2(p[o + 0], p[o + 1]), (int)pack_bf16x2(p[o + 2], p[o + 3]),
+                                (int)pack_bf16x2(p[o + 4], p[o + 5]), (int)pack_bf16x2(p[o + 6], p[o + 7])};
+  }
+}
+
+// O^T += V^T . P^T for one tile (PV waves), P^T from parity buffer `par`
+template <int S>
+__device__ __forceinline__ void pv_phase(const AttnB& c, PWave& w, int par) {
+  const int lane = c.lane, h = lane >> 5;
+  const uint8_t* tb = c.st[S];
+  const uint8_t* pb = c.p_buf + ((par * 2 + c.hg) * 64 + lane) * 32;
+  v8bf pT[2];
+  pT[0] = as_v8bf(*(const v4i*)(pb));
+  pT[1] = as_v8bf(*(const v4i*)(pb + 16));
+  if (c.flag[par * 2 + c.hg]) {
+    const float alpha = c.alpha[(par * 2 + c.hg) * 32 + (lane & 31)];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) w.acc[d] *= alpha;
+  }
+  // as in the split-dims kernel: address lane 4j+q of each 16-lane group points
+  // at row 4h + j (then + 8, + 16, + 24), dims base + 4q .. +3
+  const int a16 = lane & 15, jr = a16 >> 2, qd = a16 & 3, mh = (lane >> 4) & 1;
+  const int r0 = 4 * h + jr;
+  // base addresses for rows r0 (+16) and r0 + 8 (+16), per granule-group parity
+  const uint8_t* vb[2][2];
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int lo3 = (4 * pr + 2 * mh + (qd >> 1)) ^ swz_b(r0 + 8 * e);
+      vb[pr][e] = tb + (r0 + 8 * e) * kRowBytes + 16 * (32 * w.dh + lo3) + 8 * (qd & 1);
+    }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    v8bf va[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int off = 16 * ks * kRowBytes + 128 * (mt >> 1);
+      union { v4s h4[2]; v8bf b; } u;
+      u.h4[0] = lds_read_tr16(vb[mt & 1][0], off);
+      u.h4[1] = lds_read_tr16(vb[mt & 1][1], off);
+      va[ks] = u.b;
+    }
+    w.acc[mt] = mfma32_bf16(va[0], pT[0], w.acc[mt]);
+    w.acc[mt] = mfma32_bf16(va[1], pT[1], w.acc[mt]);
+  }
+}
+
+// PV side of pipeline step j: accumulate tile j (stage SJ)
+template <int SJ>
+__device__ __forceinline__ void pv_step(const AttnB& c, PWave& w, int j) {
+  if (j >= 0) pv_phase<SJ>(c, w, j & 1);
+  lds_barrier();
+}
+
+template <int SJ>
+__device__ __forceinline__ void g_step(const AttnB& c, const GWave& w, int j) {
+  const bool more = j + 3 < c.n_tiles;
+  if (more) issue_tile_b<(SJ + 3) % kStagesB>(c, w, j + 3);
+  if (j + 2 < c.n_tiles) {
+    if (more) wait_vm<kDmaPerB>();
+    else wait_vm<0>();
+  }
+  lds_barrier();
+}
+
+// S side of pipeline step j: score tile j+1 (stage (SJ+1)%4)
+template <int SJ>
+__device__ __forceinline__ void s_step(const AttnB& c, SWave& w, int j) {
+  if (j + 1 < c.n_tiles) s_phase<(SJ + 1) % kStagesB>(c, w, j + 1, (j + 1) & 1);
+  lds_barrier();
+}
+
+__global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
+    const uint16_t* __restrict__ q, const void* __restrict__ kv, const int32_t* __restrict__ idx,
+    int T, int L, int k, int rows_per_split, float sm_scale, uint16_t* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_st0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_st1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_st2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_st3[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[2 * 2 * 64 * 32];
+  __shared__ float s_alpha[2 * 2 * 32];
+  __shared__ int s_flag[2 * 2];
+  __shared__ int32_t s_idx[kMaxSplitRowsB];
+  __shared__ float s_ml[2 * 2 * 32];
+
+  const int qi = blockIdx.y;  // flattened (b, t)
+  const int sp = blockIdx.x;
+  const int splits = gridDim.x;
+  const int b = qi / T;
+  const int tid = threadIdx.x;
+
+  AttnB c;
+  c.st[0] = s_st0;
+  c.st[1] = s_st1;
+  c.st[2] = s_st2;
+  c.st[3] = s_st3;
+  c.p_buf = s_p;
+  c.alpha = s_alpha;
+  c.flag = s_flag;
+  c.s_idx = s_idx;
+  c.lane = tid & 63;
+  c.wave = tid >> 6;
+  const Role role = role_of(c.wave);
+  const int pw = (c.wave & 3) - 2 + 2 * (c.wave >> 2);  // PV index 0..3 for waves 2, 3, 6, 7
+  c.hg = role == kRoleS ? c.wave : (pw & 1);
+
+  const int row_begin = sp * rows_per_split;
+  const int row_end = min(k, row_begin + rows_per_split);
+  const int n_rows = row_end - row_begin;
+  c.n_tiles = (n_rows + kTileRows - 1) / kTileRows;
+
+  for (int i = tid; i < c.n_tiles * kTileRows; i += kThreadsB)
+    s_idx[i] = i < n_rows ? idx[(int64_t)qi * k + row_begin + i] : -1;
+
+  // The roles run separate code with the same sequence of barriers: one
+  // after setup, one after the prologue, one per pipeline step j = -1 ..
+  // n_tiles - 1, one before the epilogue.
+  if (role == kRoleS) {
+    SWave w;
+    w.c_log = sm_scale * kLog2e;
+    w.m_run = -INFINITY;
+    w.l_run = 0.f;
+    const uint16_t* qh = q + ((int64_t)qi * kAttHeads + 32 * c.hg + (c.lane & 31)) * kKvDim +
+                         8 * (c.lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) w.qT[ks] = as_v8bf(*(const v4i*)(qh + 16 * ks));
+    wait_vm<0>();
+    __syncthreads();
+    lds_barrier();  // prologue (tile 0 landed)
+    s_step<3>(c, w, -1);  // scores tile 0 from stage 0
+    for (int j = 0; j < c.n_tiles; j += kStagesB) {
+      s_step<0>(c, w, j);
+      if (j + 1 < c.n_tiles) s_step<1>(c, w, j + 1);
+      if (j + 2 < c.n_tiles) s_step<2>(c, w, j + 2);
+      if (j + 3 < c.n_tiles) s_step<3>(c, w, j + 3);
+    }
+    // publish each head's exponent offset and sum
+    float l_tot = w.l_run;
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (c.lane < 32) {
+      s_ml[(0 * 2 + c.hg) * 32 + c.lane] = w.m_run;
+      s_ml[(1 * 2 + c.hg) * 32 + c.lane] = l_tot;
+    }
+    __syncthreads();
+    return;
+  }
+  if (role == kRoleGather) {
+    GWave w;
+    w.g = c.wave - 4;
+    w.kv8 = (const uint8_t*)kv;
+    w.kv_b = (int64_t)b * L;
+#pragma unroll
+    for (int i = 0; i < kDmaPerB; ++i) {
+      const int o = 1024 * (w.g + kGatherWaves * i) + 16 * c.lane;  // LDS byte in the stage
+      const int r = o / kRowBytes;
+      const int pos = (o - r * kRowBytes) / 16;
+      w.dma_row[i] = r;
+      w.dma_off[i] = 16 * (pos ^ swz_b(r));
+    }
+    __syncthreads();
+    // prologue: tiles 0 and 1 in flight, wait for tile 0
+    issue_tile_b<0>(c, w, 0);
+    if (c.n_tiles > 1) {
+      issue_tile_b<1>(c, w, 1);
+      wait_vm<kDmaPerB>();
+    } else {
+      wait_vm<0>();
+    }
+    lds_barrier();
+    g_step<3>(c, w, -1);  // issues tile 2 into stage 2, waits for tile 1
+    for (int j = 0; j < c.n_tiles; j += kStagesB) {
+      g_step<0>(c, w, j);
+      if (j + 1 < c.n_tiles) g_step<1>(c, w, j + 1);
+      if (j + 2 < c.n_tiles) g_step<2>(c, w, j + 2);
+      if (j + 3 < c.n_tiles) g_step<3>(c, w, j + 3);
+    }
+    __syncthreads();
+    return;
+  }
+
+  PWave w;
+  w.dh = pw >> 1;
+#pragma unroll
+  for (int d = 0; d < 8; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w.acc[d][i] = 0.f;
+  __syncthreads();
+  lds_barrier();  // prologue
+  pv_step<3>(c, w, -1);
+  for (int j = 0; j < c.n_tiles; j += kStagesB) {
+    pv_step<0>(c, w, j);
+    if (j + 1 < c.n_tiles) pv_step<1>(c, w, j + 1);
+    if (j + 2 < c.n_tiles) pv_step<2>(c, w, j + 2);
+    if (j + 3 < c.n_tiles) pv_step<3>(c, w, j + 3);
+  }
+  __syncthreads();
+
+  const int ln = c.lane & 31, h = c.lane >> 5;
+  const float m_run = s_ml[(0 * 2 + c.hg) * 32 + ln];
+  const float l_tot = s_ml[(1 * 2 + c.hg) * 32 + ln];
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int head = 32 * c.hg + ln;
+  const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;  // log2 domain
+  // lane holds dims 256dh + 32mt + 8(i/4) + 4h + (i&3) of its head
+  if (splits == 1) {
+    uint16_t* orow = out + ((int64_t)qi * kAttHeads + head) * kLatent + 256 * w.dh + 4 * h;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const v16f& a = w.acc[mt];
+        const uint32_t lo = pack_bf16x2(a[4 * i4] * inv, a[4 * i4 + 1] * inv);
+        const uint32_t hi = pack_bf16x2(a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv);
+        *(v2i*)(orow + 32 * mt + 8 * i4) = v2i{(int)lo, (int)hi};
+      }
+    if (lse && w.dh == 0 && h == 0) lse[(int64_t)qi * kAttHeads + head] = lse2 * kLn2;
+  } else {
+    float* prow = part_o + (((int64_t)qi * splits + sp) * kAttHeads + head) * kLatent + 256 * w.dh +
+                  4 * h;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const v16f& a = w.acc[mt];
+        *(v4f*)(prow + 32 * mt + 8 * i4) =
+            v4f{a[4 * i4] * inv, a[4 * i4 + 1] * inv, a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv};
+      }
+    if (w.dh == 0 && h == 0) part_lse[((int64_t)qi * splits + sp) * kAttHeads + head] = lse2;
+  }
+}
+
 // out[q][h][:] = sum_s w_s * o_s / sum_s w_s with w_s = 2^(lse_s - max lse);
-// one workgroup per (query, group of 4 heads), consecutive threads on
-// consecutive output dims
+// one workgroup per (query, group of 4 heads), two float4 of output per
+// thread. Each thread folds the splits eight at a time with a running maximum
+// (the sum is rescaled when a larger lse appears); the eight splits' loads are
+// issued together, so a launch pays one memory latency per eight splits.
 constexpr int kCombHeads = 4;
+constexpr int kMaxCombSplits = 64;
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
                                                       int splits, uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
-  __shared__ float s_w[kCombHeads][16];
   const int qi = blockIdx.y;
   const int h0 = blockIdx.x * kCombHeads;
   const int tid = threadIdx.x;
-  if (tid < kCombHeads) {
-    const int head = h0 + tid;
-    float mx = -INFINITY;
-    for (int s = 0; s < splits; ++s)
-      mx = fmaxf(mx, part_lse[((int64_t)qi * splits + s) * kAttHeads + head]);
-    float wts[16];
-    float wsum = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float l = part_lse[((int64_t)qi * splits + s) * kAttHeads + head];
-      wts[s] = (l == -INFINITY) ? 0.f : exp2f(l - mx);
-      wsum += wts[s];
-    }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    for (int s = 0; s < splits; ++s) s_w[tid][s] = wts[s] * inv;
-    if (lse) lse[(int64_t)qi * kAttHeads + head] = wsum > 0.f ? (mx + log2f(wsum)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
   const int64_t per_split = (int64_t)kAttHeads * kLatent;
   const float* base = part_o + (int64_t)qi * splits * per_split + (int64_t)h0 * kLatent;
+  const float* lbase = part_lse + (int64_t)qi * splits * kAttHeads + h0;
   uint16_t* obase = out + (int64_t)qi * per_split + (int64_t)h0 * kLatent;
-  for (int i = tid; i < kCombHeads * kLatent / 4; i += 256) {
-    const int e = 4 * i;
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int e = 4 * (tid + 256 * rep);  // element in the 4 heads x 512 dims block
     const int hl = e / kLatent;
-    v4f a = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s) a += *(const v4f*)(base + s * per_split + e) * s_w[hl][s];
-    *(v2i*)(obase + e) = v2i{(int)pack_bf16x2(a[0], a[1]), (int)pack_bf16x2(a[2], a[3])};
+    float m = -INFINITY, wsum = 0.f;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+      // eight splits' loads at once (indices past the end re-read the last
+      // split and are masked)
+      float l[8];
+      v4f o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sp = min(sp0 + j, splits - 1);
+        l[j] = lbase[sp * kAttHeads + hl];
+        o[j] = *(const v4f*)(base + sp * per_split + e);
+      }
+      float m_new = m;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (sp0 + j >= splits) l[j] = -INFINITY;
+        m_new = fmaxf(m_new, l[j]);
+      }
+      if (m_new == -INFINITY) continue;  // no valid row in these splits yet
+      const float sc = m == -INFINITY ? 0.f : exp2f(m - m_new);
+      acc *= sc;
+      wsum *= sc;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float w = l[j] == -INFINITY ? 0.f : exp2f(l[j] - m_new);
+        acc += o[j] * w;
+        wsum += w;
+      }
+      m = m_new;
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    acc *= inv;
+    *(v2i*)(obase + e) = v2i{(int)pack_bf16x2(acc[0], acc[1]), (int)pack_bf16x2(acc[2], acc[3])};
+    if (lse && (e & (kLatent - 1)) == 0)
+      lse[(int64_t)qi * kAttHeads + h0 + hl] = wsum > 0.f ? (m + log2f(wsum)) * kLn2 : -INFINITY;
   }
 }
 
 }  // namespace
 
 size_t attn_workspace_bytes(int64_t queries, int k) {
-  const SplitPlan p = plan_splits(queries, k);
-  if (p.splits <= 1) return 0;
-  size_t o = (size_t)queries * p.splits * kAttHeads * kLatent * sizeof(float);
-  size_t l = (size_t)queries * p.splits * kAttHeads * sizeof(float);
+  // the larger of the two kernels' split plans (the size query has no KV type)
+  const SplitPlan pa = plan_splits(queries, k);
+  const SplitPlan pb = plan_splits_b(queries, k);
+  const int splits = pa.splits > pb.splits ? pa.splits : pb.splits;
+  if (splits <= 1) return 0;
+  size_t o = (size_t)queries * splits * kAttHeads * kLatent * sizeof(float);
+  size_t l = (size_t)queries * splits * kAttHeads * sizeof(float);
   return o + l;
 }
 
@@ -487,7 +928,7 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
                              int k, float sm_scale, uint16_t* out, float* lse,
                              void* workspace, hipStream_t stream) {
   const int64_t queries = (int64_t)B * T;
-  const SplitPlan p = plan_splits(queries, k);
+  const SplitPlan p = kv_fp8 ? plan_splits(queries, k) : plan_splits_b(queries, k);
   float* part_o = nullptr;
   float* part_lse = nullptr;
   if (p.splits > 1) {
@@ -500,12 +941,12 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
     e = launch_kernel(sparse_mla_kernel<true>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx, T,
                       L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
   else
-    e = launch_kernel(sparse_mla_kernel<false>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx,
-                      T, L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
+    e = launch_kernel(sparse_mla_b_kernel, grid, dim3(kThreadsB), 0, stream, q, kv, idx, T, L, k,
+                      p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
   if (e != hipSuccess || p.splits <= 1) return e;
   return launch_kernel(combine_kernel, dim3(kAttHeads / kCombHeads, (unsigned)queries), dim3(256), 0,
-                       stream, part_o,
-                       part_lse, p.splits, out, lse);
+                       stream, part_o, part_lse, p.splits, out, lse);
 }
 
 }  // namespace lcs
+
