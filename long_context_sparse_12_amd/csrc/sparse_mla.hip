@@ -37,13 +37,16 @@ struct SplitPlan {
 #ifndef LCS_ATTN_TARGET_WGS
 #define LCS_ATTN_TARGET_WGS 256  // about one workgroup per CU
 #endif
+#ifndef LCS_ATTN_MAX_SPLITS
+#define LCS_ATTN_MAX_SPLITS 64
+#endif
 
 __host__ __device__ inline SplitPlan plan_splits(int64_t queries, int k) {
   SplitPlan p;
   int64_t s = (LCS_ATTN_TARGET_WGS + queries - 1) / queries;
   const int64_t max_s = (k + kTileRows - 1) / kTileRows;
   if (s > max_s) s = max_s;
-  if (s > 16) s = 16;
+  if (s > LCS_ATTN_MAX_SPLITS) s = LCS_ATTN_MAX_SPLITS;
   if (s < 1) s = 1;
   int64_t r = (k + s - 1) / s;
   r = (r + kTileRows - 1) / kTileRows * kTileRows;

@@ -18,10 +18,11 @@
 //           bucket b1 holding the k-th largest key, then writes, in position
 //           order, the positions whose bucket is above b1 ("sure") or equal to
 //           b1 ("candidate") into its slice of the row's list
-//   final : one workgroup per row resolves the candidates with two more digits
-//           (12 + 8 bits) in LDS, which fixes the exact threshold key tau and
-//           how many keys equal to tau are kept (the lowest positions), then
-//           emits the selection in position order.
+//   final : one workgroup per row stages the row's entries and candidate
+//           keys in LDS (up to 16384; more are read from global memory), resolves
+//           the candidates with two more digits (12 + 8 bits), which fixes the
+//           exact threshold key tau and how many keys equal to tau are kept
+//           (the lowest positions), then emits the selection in position order.
 // Scores are read twice plus one gather per candidate.
 #include "common.h"
 
@@ -236,6 +237,35 @@ __global__ void __launch_bounds__(kThreads) topk_filter_kernel(
   if (tid == 0) counts[(size_t)row * chunks + blockIdx.x] = written;
 }
 
+// Block-wide exclusive prefix of one uint32 per thread: an inclusive scan
+// inside each wave (shuffles), then the wave totals through LDS (s_tmp holds
+// kWavesTk entries). Returns the exclusive prefix; total in `tot`.
+__device__ uint32_t block_prefix(uint32_t v, uint32_t* s_tmp, uint32_t& tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t up = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += up;
+  }
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWavesTk; ++i) {
+    const uint32_t t = s_tmp[i];
+    before += i < wave ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  return before + incl - v;
+}
+
+// Candidates a row can stage in LDS for the fast path of the final kernel
+constexpr int kStage = 16384;
+constexpr int kStagePer = kStage / kThreads;  // 16 entries per thread
+
 __global__ void __launch_bounds__(kThreads) topk_final_kernel(
     const float* __restrict__ scores, int L, int k, int chunks, int chunk,
     const RowState* __restrict__ state, const uint32_t* __restrict__ counts,
@@ -245,6 +275,8 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
   __shared__ uint32_t s_scan[kThreads + kWavesTk];
   __shared__ uint32_t s_out[2];
   __shared__ uint32_t s_pref[1024 + 1];
+  __shared__ uint32_t s_ent[kStage];  // entries (position | sure flag), in position order
+  __shared__ uint32_t s_key[kStage];  // their keys (candidates only)
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const RowState st = state[row];
@@ -253,35 +285,81 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
   const float* srow = scores + (size_t)row * L;
   int32_t* out = idx + (size_t)row * k;
   const uint32_t* list = lists + (size_t)row * chunks * (size_t)chunk;
-  // chunk offsets in the concatenated entry list
-  for (int c = tid; c < chunks; c += kThreads) s_pref[c] = counts[(size_t)row * chunks + c];
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int c = 0; c < chunks; ++c) {
-      const uint32_t v = s_pref[c];
-      s_pref[c] = run;
-      run += v;
-    }
-    s_pref[chunks] = run;
+  // chunk offsets in the concatenated entry list (chunks <= 2 * kThreads)
+  {
+    const int c0 = 2 * tid;
+    const uint32_t v0 = c0 < chunks ? counts[(size_t)row * chunks + c0] : 0u;
+    const uint32_t v1 = c0 + 1 < chunks ? counts[(size_t)row * chunks + c0 + 1] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_prefix(v0 + v1, s_scan, tot);
+    if (c0 < chunks) s_pref[c0] = ex;
+    if (c0 + 1 < chunks) s_pref[c0 + 1] = ex + v0;
+    if (tid == 0) s_pref[chunks] = tot;
+    __syncthreads();
   }
-  __syncthreads();
   const uint32_t n_ent = s_pref[chunks];
   const uint32_t n_above = st.n_above;
-  auto entry = [&](uint32_t e) -> uint32_t {
+  auto chunk_of = [&](uint32_t e) -> int {
     int lo = 0, hi = chunks - 1;  // last chunk with s_pref[c] <= e
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_pref[mid] <= e) lo = mid; else hi = mid - 1;
     }
-    return list[(size_t)lo * chunk + (e - s_pref[lo])];
+    return lo;
+  };
+  auto entry = [&](uint32_t e) -> uint32_t {
+    const int c = chunk_of(e);
+    return list[(size_t)c * chunk + (e - s_pref[c])];
+  };
+  const bool staged = n_ent <= (uint32_t)kStage;
+  if (staged) {
+    // Stage every entry and candidate key in LDS with all global loads of a
+    // thread in flight together (one latency for the entries, one for keys).
+    // The source offset of every entry is first written chunk by chunk into
+    // s_key (LDS only), then read back by entry.
+    for (int c = tid; c < chunks; c += kThreads) {
+      const uint32_t p0 = s_pref[c], n = s_pref[c + 1] - p0;
+      for (uint32_t i = 0; i < n; ++i) s_key[p0 + i] = (uint32_t)c * chunk + i;
+    }
+    __syncthreads();
+    uint32_t v[kStagePer];
+#pragma unroll
+    for (int j = 0; j < kStagePer; ++j) {
+      const uint32_t e = tid + kThreads * j;
+      v[j] = e < n_ent ? list[s_key[e]] : 0u;
+    }
+    float f[kStagePer];
+#pragma unroll
+    for (int j = 0; j < kStagePer; ++j) {
+      const uint32_t e = tid + kThreads * j;
+      f[j] = (e < n_ent && !(v[j] & kSure)) ? srow[v[j] & ~kSure] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kStagePer; ++j) {
+      const uint32_t e = tid + kThreads * j;
+      if (e < n_ent) {
+        s_ent[e] = v[j];
+        s_key[e] = score_key(f[j]);
+      }
+    }
+  }
+  // entry e and its key (valid for candidates only)
+  auto get = [&](uint32_t e, uint32_t& key) -> uint32_t {
+    if (staged) {
+      key = s_key[e];
+      return s_ent[e];
+    }
+    const uint32_t v = entry(e);
+    key = (v & kSure) ? 0u : score_key(srow[v]);
+    return v;
   };
   // digit 2 over the candidates
   for (int i = tid; i < kBins2; i += kThreads) hist[i] = 0;
   __syncthreads();
   for (uint32_t e = tid; e < n_ent; e += kThreads) {
-    const uint32_t v = entry(e);
-    if (!(v & kSure)) atomicAdd(&hist[(score_key(srow[v]) >> 8) & 0xFFFu], 1u);
+    uint32_t key;
+    const uint32_t v = get(e, key);
+    if (!(v & kSure)) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
   }
   __syncthreads();
   const uint32_t need1 = (uint32_t)k - n_above;
@@ -294,11 +372,9 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
   __syncthreads();
   const uint32_t pre12 = (b1 << 12) | b2;
   for (uint32_t e = tid; e < n_ent; e += kThreads) {
-    const uint32_t v = entry(e);
-    if (!(v & kSure)) {
-      const uint32_t key = score_key(srow[v]);
-      if ((key >> 8) == pre12) atomicAdd(&hist[key & 0xFFu], 1u);
-    }
+    uint32_t key;
+    const uint32_t v = get(e, key);
+    if (!(v & kSure) && (key >> 8) == pre12) atomicAdd(&hist[key & 0xFFu], 1u);
   }
   __syncthreads();
   const uint32_t need2 = need1 - above2;
@@ -308,31 +384,49 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
   const uint32_t tau = (pre12 << 8) | b3;
   const uint32_t need_tie = need2 - above3;  // keys equal to tau that are kept
   __syncthreads();
-  // ordered emission
+  // ordered emission, four consecutive entries per thread per block
   uint32_t ties_before = 0, sel_before = 0;
   int parity = 0;
-  for (uint32_t base = 0; base < n_ent; base += kThreads) {
-    const uint32_t e = base + tid;
-    uint32_t is_gt = 0, is_tie = 0, s = 0;
-    if (e < n_ent) {
-      const uint32_t v = entry(e);
-      s = v & ~kSure;
-      if (v & kSure) {
-        is_gt = 1;
-      } else {
-        const uint32_t key = score_key(srow[s]);
-        is_gt = key > tau;
-        is_tie = key == tau;
+  for (uint32_t base = 0; base < n_ent; base += 4 * kThreads) {
+    uint32_t pos4[4], gt4[4], tie4[4];
+    uint32_t n_tie = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t e = base + 4 * tid + j;
+      gt4[j] = tie4[j] = 0;
+      pos4[j] = 0;
+      if (e < n_ent) {
+        uint32_t key;
+        const uint32_t v = get(e, key);
+        pos4[j] = v & ~kSure;
+        if (v & kSure) {
+          gt4[j] = 1;
+        } else {
+          gt4[j] = key > tau;
+          tie4[j] = key == tau;
+        }
       }
+      n_tie += tie4[j];
     }
     uint32_t tie_tot;
-    const uint32_t tie_rank = ties_before + block_prefix_small(is_tie, s_wave, parity, tie_tot);
+    uint32_t tie_rank = ties_before + block_prefix_small(n_tie, s_wave, parity, tie_tot);
     parity ^= 1;
-    const uint32_t sel = is_gt | (is_tie & (tie_rank < need_tie ? 1u : 0u));
+    uint32_t sel4[4], n_sel = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sel4[j] = gt4[j] | (tie4[j] & (tie_rank < need_tie ? 1u : 0u));
+      tie_rank += tie4[j];
+      n_sel += sel4[j];
+    }
     uint32_t sel_tot;
-    const uint32_t pos = sel_before + block_prefix_small(sel, s_wave, parity, sel_tot);
+    uint32_t pos = sel_before + block_prefix_small(n_sel, s_wave, parity, sel_tot);
     parity ^= 1;
-    if (sel && pos < (uint32_t)k) out[pos] = (int32_t)s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (sel4[j]) {
+        if (pos < (uint32_t)k) out[pos] = (int32_t)pos4[j];
+        ++pos;
+      }
     ties_before += tie_tot;
     sel_before += sel_tot;
   }
