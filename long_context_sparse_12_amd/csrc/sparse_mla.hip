@@ -520,9 +520,8 @@ struct PWave {
 };
 
 struct GWave {
-  int g;  // 0 or 1
-  const uint8_t* kv8;
-  int64_t kv_b;
+  int g;                // 0 or 1 (wave-uniform)
+  const uint8_t* kvb;   // this sequence's rows: kv + b * L * 1152
   int dma_row[kDmaPerB];  // row inside the tile of each gather
   int dma_off[kDmaPerB];  // byte offset inside the row (swizzled granule)
 };
@@ -536,8 +535,9 @@ __device__ __forceinline__ void issue_tile_b(const AttnB& c, const GWave& w, int
   for (int i = 0; i < kDmaPerB; ++i) rows[i] = c.s_idx[tile * kTileRows + w.dma_row[i]];
 #pragma unroll
   for (int i = 0; i < kDmaPerB; ++i) {
-    const int32_t s = rows[i] >= 0 ? rows[i] : 0;  // padding rows load row 0 (masked)
-    dma16(w.kv8 + (w.kv_b + s) * (int64_t)kRowBytes + w.dma_off[i],
+    const uint32_t s = rows[i] >= 0 ? (uint32_t)rows[i] : 0u;  // padding rows load row 0 (masked)
+    // 32-bit offset from the sequence base (the launcher keeps L * 1152 < 2^32)
+    dma16(w.kvb + (s * (uint32_t)kRowBytes + (uint32_t)w.dma_off[i]),
           c.st[S] + 1024 * (w.g + kGatherWaves * i));
   }
 }
@@ -578,11 +578,13 @@ __device__ __forceinline__ void s_phase(const AttnB& c, SWave& w, int tile, int 
   // validity of the tile's rows as a wave-uniform bit mask (bit r: row r has
   // a position); a tile without padding skips the masking
   const uint32_t valid = (uint32_t)__ballot(c.s_idx[tile * kTileRows + ln] >= 0);
-  // lane holds head 32hg + (lane&31) for rows 8(i/4) + 4h + (i&3)
+  // lane holds head 32hg + (lane&31) for rows 8(i/4) + 4h + (i&3); raw dot
+  // products here, the scale enters through the exponent's FMA below
   float t[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) t[i] = (se[i] + so[i]) * w.c_log;
-  if (valid != 0xFFFFFFFFu) {
+  for (int i = 0; i < 16; ++i) t[i] = se[i] + so[i];
+  const bool all_valid = valid == 0xFFFFFFFFu;
+  if (!all_valid) {
     const uint32_t mine = valid >> (4 * h);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -594,17 +596,26 @@ __device__ __forceinline__ void s_phase(const AttnB& c, SWave& w, int tile, int 
   {
     // the other lane half holds the same head's other 16 rows
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * w.c_log;  // log2 domain
   }
   // lazy rescaling, as in the split-dims kernel above
   const bool first = w.m_run == -INFINITY;
   const float m_new = (first || mx > w.m_run + kRescaleSlack) ? mx : w.m_run;
   float p[16];
   float psum = 0.f;
+  if (all_valid) {
+    // m_new is finite: exp2(x * c - m) of every row
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    p[i] = (t[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(t[i] - m_new);
-    psum += p[i];
+    for (int i = 0; i < 16; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(fmaf(t[i], w.c_log, -m_new));
+      psum += p[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = (t[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(fmaf(t[i], w.c_log, -m_new));
+      psum += p[i];
+    }
   }
   const bool rescale = __ballot(!first && m_new != w.m_run) != 0;
   if (rescale) {
@@ -769,9 +780,8 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   }
   if (role == kRoleGather) {
     GWave w;
-    w.g = c.wave - 4;
-    w.kv8 = (const uint8_t*)kv;
-    w.kv_b = (int64_t)b * L;
+    w.g = __builtin_amdgcn_readfirstlane(c.wave - 4);
+    w.kvb = (const uint8_t*)kv + (int64_t)b * L * kRowBytes;
 #pragma unroll
     for (int i = 0; i < kDmaPerB; ++i) {
       const int o = 1024 * (w.g + kGatherWaves * i) + 16 * c.lane;  // LDS byte in the stage
@@ -931,7 +941,9 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
                              int k, float sm_scale, uint16_t* out, float* lse,
                              void* workspace, hipStream_t stream) {
   const int64_t queries = (int64_t)B * T;
-  const SplitPlan p = kv_fp8 ? plan_splits(queries, k) : plan_splits_b(queries, k);
+  // the split-role kernel addresses a sequence's rows with 32-bit offsets
+  const bool role_kernel = !kv_fp8 && (int64_t)L * kRowBytes < ((int64_t)1 << 32);
+  const SplitPlan p = role_kernel ? plan_splits_b(queries, k) : plan_splits(queries, k);
   float* part_o = nullptr;
   float* part_lse = nullptr;
   if (p.splits > 1) {
@@ -943,9 +955,12 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
   if (kv_fp8)
     e = launch_kernel(sparse_mla_kernel<true>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx, T,
                       L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
-  else
+  else if (role_kernel)
     e = launch_kernel(sparse_mla_b_kernel, grid, dim3(kThreadsB), 0, stream, q, kv, idx, T, L, k,
                       p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
+  else
+    e = launch_kernel(sparse_mla_kernel<false>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx,
+                      T, L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
   if (e != hipSuccess || p.splits <= 1) return e;
   return launch_kernel(combine_kernel, dim3(kAttHeads / kCombHeads, (unsigned)queries), dim3(256), 0,
                        stream, part_o, part_lse, p.splits, out, lse);
