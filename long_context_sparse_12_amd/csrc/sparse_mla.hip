@@ -38,7 +38,7 @@ struct SplitPlan {
 #define LCS_ATTN_TARGET_WGS 256  // about one workgroup per CU
 #endif
 #ifndef LCS_ATTN_MAX_SPLITS
-#define LCS_ATTN_MAX_SPLITS 64
+#define LCS_ATTN_MAX_SPLITS 32
 #endif
 
 __host__ __device__ inline SplitPlan plan_splits(int64_t queries, int k) {
