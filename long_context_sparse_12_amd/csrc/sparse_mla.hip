@@ -452,7 +452,6 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
 constexpr int kWavesB = 8;
 constexpr int kThreadsB = 64 * kWavesB;
 constexpr int kStagesB = 4;
-constexpr int kMaxSplitRowsB = 512;
 constexpr int kGatherWaves = 2;
 constexpr int kDmaPerB = kTileBytes / 1024 / kGatherWaves;  // 18 gathers per lane per tile
 
@@ -474,11 +473,9 @@ __device__ __forceinline__ Role role_of(int wave) {
 __host__ __device__ inline SplitPlan plan_splits_b(int64_t queries, int k) {
   SplitPlan p;
   int64_t s = (LCS_ATTN_B_TARGET_WGS + queries - 1) / queries;
-  const int64_t min_s = (k + kMaxSplitRowsB - 1) / kMaxSplitRowsB;
   const int64_t max_s = (k + kTileRows - 1) / kTileRows;
   if (s > max_s) s = max_s;
   if (s > LCS_ATTN_B_MAX_SPLITS) s = LCS_ATTN_B_MAX_SPLITS;
-  if (s < min_s) s = min_s;
   if (s < 1) s = 1;
   int64_t r = (k + s - 1) / s;
   r = (r + kTileRows - 1) / kTileRows * kTileRows;
@@ -503,15 +500,40 @@ struct AttnB {
   uint8_t* p_buf;   // [2 parity][2 hg][64 lanes][32 B]  P^T B operands
   float* alpha;     // [2 parity][2 hg][32 heads]
   int* flag;        // [2 parity][2 hg]
-  const int32_t* s_idx;
-  int n_tiles;
+  int32_t* ring;    // [4 slots][32 rows]  positions of the tiles t with t & 3 = slot
+  const int32_t* idx_q;  // this split's selected positions (global memory)
+  int n_rows, n_tiles;
   int wave, lane, hg;
 };
+
+// A split may hold all k selected rows, so its positions do not sit in LDS
+// at once: S wave 0 streams them, one tile per pipeline step, into a ring of
+// four 32-entry slots (tile t in slot t & 3, -1 for padding and for rows past
+// the split's end). Only that wave loads positions into registers; the gather
+// waves read them from the ring and issue nothing but global->LDS copies, so
+// their waits count copies alone (loads into registers in flight beside the
+// copies would make the compiler wait for all of them before any use).
+constexpr int kPosSlots = 4;
+__device__ __forceinline__ int32_t* pos_slot(const AttnB& c, int tile) {
+  return c.ring + (tile & (kPosSlots - 1)) * kTileRows;
+}
+
+// position of row (lane & 31) of `tile` (rows past the end read the split's
+// last entry, a valid address; ring_put masks them)
+__device__ __forceinline__ int32_t load_pos(const AttnB& c, int tile) {
+  return c.idx_q[min(tile * kTileRows + (c.lane & 31), c.n_rows - 1)];
+}
+
+__device__ __forceinline__ void ring_put(const AttnB& c, int tile, int32_t p) {
+  const int r = tile * kTileRows + (c.lane & 31);
+  if (c.lane < kTileRows) pos_slot(c, tile)[c.lane] = r < c.n_rows ? p : -1;
+}
 
 struct SWave {
   v8bf qT[36];  // Q^T: head 32hg + (lane&31), dims 16ks + 8(lane>>5) .. +8
   float c_log;
   float m_run, l_run;
+  int32_t pn;  // S wave 0: positions of the next tile to enter the ring
 };
 
 struct PWave {
@@ -532,7 +554,7 @@ template <int S>
 __device__ __forceinline__ void issue_tile_b(const AttnB& c, const GWave& w, int tile) {
   int32_t rows[kDmaPerB];
 #pragma unroll
-  for (int i = 0; i < kDmaPerB; ++i) rows[i] = c.s_idx[tile * kTileRows + w.dma_row[i]];
+  for (int i = 0; i < kDmaPerB; ++i) rows[i] = pos_slot(c, tile)[w.dma_row[i]];
 #pragma unroll
   for (int i = 0; i < kDmaPerB; ++i) {
     const uint32_t s = rows[i] >= 0 ? (uint32_t)rows[i] : 0u;  // padding rows load row 0 (masked)
@@ -577,7 +599,7 @@ __device__ __forceinline__ void s_phase(const AttnB& c, SWave& w, int tile, int 
   }
   // validity of the tile's rows as a wave-uniform bit mask (bit r: row r has
   // a position); a tile without padding skips the masking
-  const uint32_t valid = (uint32_t)__ballot(c.s_idx[tile * kTileRows + ln] >= 0);
+  const uint32_t valid = (uint32_t)__ballot(pos_slot(c, tile)[ln] >= 0);
   // lane holds head 32hg + (lane&31) for rows 8(i/4) + 4h + (i&3); raw dot
   // products here, the scale enters through the exponent's FMA below
   float t[16];
@@ -696,9 +718,16 @@ __device__ __forceinline__ void g_step(const AttnB& c, const GWave& w, int j) {
   lds_barrier();
 }
 
-// S side of pipeline step j: score tile j+1 (stage (SJ+1)%4)
+// S side of pipeline step j: S wave 0 puts tile j+4's positions (loaded one
+// step earlier) into the ring slot of tile j (read for the last time in step
+// j-1) and loads tile j+5's; then score tile j+1 (stage (SJ+1)%4). The gather
+// waves read tile j+4's slot in step j+1, after this step's barrier.
 template <int SJ>
 __device__ __forceinline__ void s_step(const AttnB& c, SWave& w, int j) {
+  if (c.wave == 0) {
+    ring_put(c, j + 4, w.pn);
+    w.pn = load_pos(c, j + 5);
+  }
   if (j + 1 < c.n_tiles) s_phase<(SJ + 1) % kStagesB>(c, w, j + 1, (j + 1) & 1);
   lds_barrier();
 }
@@ -714,7 +743,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t s_p[2 * 2 * 64 * 32];
   __shared__ float s_alpha[2 * 2 * 32];
   __shared__ int s_flag[2 * 2];
-  __shared__ int32_t s_idx[kMaxSplitRowsB];
+  __shared__ int32_t s_ring[kPosSlots * kTileRows];
   __shared__ float s_ml[2 * 2 * 32];
 
   const int qi = blockIdx.y;  // flattened (b, t)
@@ -731,7 +760,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   c.p_buf = s_p;
   c.alpha = s_alpha;
   c.flag = s_flag;
-  c.s_idx = s_idx;
+  c.ring = s_ring;
   c.lane = tid & 63;
   c.wave = tid >> 6;
   const Role role = role_of(c.wave);
@@ -740,11 +769,9 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
 
   const int row_begin = sp * rows_per_split;
   const int row_end = min(k, row_begin + rows_per_split);
-  const int n_rows = row_end - row_begin;
-  c.n_tiles = (n_rows + kTileRows - 1) / kTileRows;
-
-  for (int i = tid; i < c.n_tiles * kTileRows; i += kThreadsB)
-    s_idx[i] = i < n_rows ? idx[(int64_t)qi * k + row_begin + i] : -1;
+  c.n_rows = row_end - row_begin;
+  c.n_tiles = (c.n_rows + kTileRows - 1) / kTileRows;
+  c.idx_q = idx + (int64_t)qi * k + row_begin;
 
   // The roles run separate code with the same sequence of barriers: one
   // after setup, one after the prologue, one per pipeline step j = -1 ..
@@ -758,6 +785,14 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
                          8 * (c.lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) w.qT[ks] = as_v8bf(*(const v4i*)(qh + 16 * ks));
+    if (c.wave == 0) {
+      // tiles 0..2 into the ring before the gathers start; tile 3 goes in at step -1
+      const int32_t p0 = load_pos(c, 0), p1 = load_pos(c, 1), p2 = load_pos(c, 2);
+      w.pn = load_pos(c, 3);
+      ring_put(c, 0, p0);
+      ring_put(c, 1, p1);
+      ring_put(c, 2, p2);
+    }
     wait_vm<0>();
     __syncthreads();
     lds_barrier();  // prologue (tile 0 landed)
