@@ -369,12 +369,9 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
   const int n_rows = row_end - row_begin;
   c.n_tiles = (n_rows + kTileRows - 1) / kTileRows;
 
-  // selected positions (and FP8 row scales) of this split; -1 for padding
-  for (int i = tid; i < c.n_tiles * kTileRows; i += kThreadsA) {
-    const int32_t s = i < n_rows ? idx[(int64_t)qi * k + row_begin + i] : -1;
-    s_idx[i] = s;
-    if (FP8) s_scl[i] = s >= 0 ? kv_scale[(int64_t)b * L + s] : 0.f;
-  }
+  // selected positions of this split; -1 for padding
+  for (int i = tid; i < c.n_tiles * kTileRows; i += kThreadsA)
+    s_idx[i] = i < n_rows ? idx[(int64_t)qi * k + row_begin + i] : -1;
   // Q^T as the B operand: lane holds head 32hg + (lane&31), dims 144dq + 16ks + 8(lane>>5) .. +8
   {
     const uint16_t* qh = q + ((int64_t)qi * kAttHeads + 32 * c.hg + (c.lane & 31)) * kKvDim +
@@ -390,8 +387,28 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
   __syncthreads();
 
   static_assert(kStages == 3, "the loop below is unrolled for three stages");
+  // FP8 row scales: their loads depend on the positions just published, so
+  // they go out together with the first two tiles' gathers (one memory
+  // latency for both) and reach LDS before the first tile step's barrier
+  constexpr int kSclPer = kMaxSplitRows / kThreadsA;
+  float scl[FP8 ? kSclPer : 1];
+  if (FP8) {
+#pragma unroll
+    for (int u = 0; u < kSclPer; ++u) {
+      const int i = tid + kThreadsA * u;
+      const int32_t s = i < c.n_tiles * kTileRows ? s_idx[i] : -1;
+      scl[u] = s >= 0 ? kv_scale[(int64_t)b * L + s] : 0.f;
+    }
+  }
   if (c.n_tiles > 0) issue_tile<FP8, 0>(c, 0);
   if (c.n_tiles > 1) issue_tile<FP8, 1>(c, 1);
+  if (FP8) {
+#pragma unroll
+    for (int u = 0; u < kSclPer; ++u) {
+      const int i = tid + kThreadsA * u;
+      if (i < c.n_tiles * kTileRows) s_scl[i] = scl[u];
+    }
+  }
   for (int tile = 0; tile < c.n_tiles; tile += kStages) {
     tile_step<FP8, 0>(c, tile, tid);
     if (tile + 1 < c.n_tiles) tile_step<FP8, 1>(c, tile + 1, tid);
@@ -897,65 +914,92 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   }
 }
 
-// out[q][h][:] = sum_s w_s * o_s / sum_s w_s with w_s = 2^(lse_s - max lse);
-// one workgroup per (query, group of 4 heads), two float4 of output per
-// thread. Each thread folds the splits eight at a time with a running maximum
-// (the sum is rescaled when a larger lse appears); the eight splits' loads are
-// issued together, so a launch pays one memory latency per eight splits.
-constexpr int kCombHeads = 4;
-constexpr int kMaxCombSplits = 64;
+// out[q][h][:] = sum_s w_s * o_s / sum_s w_s with w_s = 2^(lse_s - max lse)
+// (log2 domain). 256 threads per workgroup = G split groups x 256/G columns
+// of four output elements; a workgroup covers 1024/G consecutive elements of
+// a query's [64 heads][512] output, so a query spreads over 32 G workgroups.
+// Group g folds splits g, g + G, g + 2G, ... with a running maximum, the
+// loads of up to eight of its splits in flight at a time; with G > 1 the
+// groups' partial states then merge through LDS. G = 1 serves up to eight
+// splits in one memory latency per thread, G = 4 up to 32.
+constexpr int kCombBatch = 8;
+template <int G>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
                                                       int splits, uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
+  constexpr int kCols = 256 / G;
+  __shared__ v4f s_acc[G > 1 ? G - 1 : 1][kCols];
+  __shared__ float s_m[G], s_w[G];
   const int qi = blockIdx.y;
-  const int h0 = blockIdx.x * kCombHeads;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, grp = tid / kCols, col = tid % kCols;
   const int64_t per_split = (int64_t)kAttHeads * kLatent;
-  const float* base = part_o + (int64_t)qi * splits * per_split + (int64_t)h0 * kLatent;
-  const float* lbase = part_lse + (int64_t)qi * splits * kAttHeads + h0;
-  uint16_t* obase = out + (int64_t)qi * per_split + (int64_t)h0 * kLatent;
+  const int e = blockIdx.x * (4 * kCols) + 4 * col;  // element within a split's output
+  const int head = e / kLatent;
+  const float* base = part_o + (int64_t)qi * splits * per_split + e;
+  const float* lbase = part_lse + (int64_t)qi * splits * kAttHeads + head;
+  float m = -INFINITY, wsum = 0.f;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = grp; s0 < splits; s0 += G * kCombBatch) {
+    const int nb = min(kCombBatch, (splits - s0 + G - 1) / G);  // this group's splits in the batch
+    float l[kCombBatch];
+    v4f o[kCombBatch];
 #pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int e = 4 * (tid + 256 * rep);  // element in the 4 heads x 512 dims block
-    const int hl = e / kLatent;
-    float m = -INFINITY, wsum = 0.f;
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
-      // eight splits' loads at once (indices past the end re-read the last
-      // split and are masked)
-      float l[8];
-      v4f o[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sp = min(sp0 + j, splits - 1);
-        l[j] = lbase[sp * kAttHeads + hl];
-        o[j] = *(const v4f*)(base + sp * per_split + e);
+    for (int j = 0; j < kCombBatch; ++j) {
+      l[j] = -INFINITY;
+      o[j] = v4f{0.f, 0.f, 0.f, 0.f};
+      if (j < nb) {
+        const int64_t sp = s0 + G * j;
+        l[j] = lbase[sp * kAttHeads];
+        o[j] = *(const v4f*)(base + sp * per_split);
       }
-      float m_new = m;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (sp0 + j >= splits) l[j] = -INFINITY;
-        m_new = fmaxf(m_new, l[j]);
-      }
-      if (m_new == -INFINITY) continue;  // no valid row in these splits yet
-      const float sc = m == -INFINITY ? 0.f : exp2f(m - m_new);
-      acc *= sc;
-      wsum *= sc;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float w = l[j] == -INFINITY ? 0.f : exp2f(l[j] - m_new);
-        acc += o[j] * w;
-        wsum += w;
-      }
-      m = m_new;
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    acc *= inv;
-    *(v2i*)(obase + e) = v2i{(int)pack_bf16x2(acc[0], acc[1]), (int)pack_bf16x2(acc[2], acc[3])};
-    if (lse && (e & (kLatent - 1)) == 0)
-      lse[(int64_t)qi * kAttHeads + h0 + hl] = wsum > 0.f ? (m + log2f(wsum)) * kLn2 : -INFINITY;
+    float m_new = m;
+#pragma unroll
+    for (int j = 0; j < kCombBatch; ++j) m_new = fmaxf(m_new, l[j]);
+    if (m_new == -INFINITY) continue;  // no valid row in these splits yet
+    const float sc = m == -INFINITY ? 0.f : exp2f(m - m_new);
+    acc *= sc;
+    wsum *= sc;
+#pragma unroll
+    for (int j = 0; j < kCombBatch; ++j) {
+      const float w = l[j] == -INFINITY ? 0.f : exp2f(l[j] - m_new);
+      acc += o[j] * w;
+      wsum += w;
+    }
+    m = m_new;
   }
+  float mx = m, wt = wsum;
+  v4f o = acc;
+  if (G > 1) {
+    // the threads of a group that serve one head hold the same m and wsum
+    // (they depend on that head's lse values only); a workgroup spans one head
+    if (grp > 0) s_acc[grp - 1][col] = acc;
+    if (col == 0) {
+      s_m[grp] = m;
+      s_w[grp] = wsum;
+    }
+    __syncthreads();
+    if (grp != 0) return;
+    mx = s_m[0];
+#pragma unroll
+    for (int g = 1; g < G; ++g) mx = fmaxf(mx, s_m[g]);
+    wt = 0.f;
+    o = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mg = s_m[g];
+      const float f = mg == -INFINITY ? 0.f : exp2f(mg - mx);
+      wt += s_w[g] * f;
+      o += (g == 0 ? acc : s_acc[g > 0 ? g - 1 : 0][col]) * f;
+    }
+  }
+  const float inv = wt > 0.f ? 1.f / wt : 0.f;
+  o *= inv;
+  *(v2i*)(out + (int64_t)qi * per_split + e) =
+      v2i{(int)pack_bf16x2(o[0], o[1]), (int)pack_bf16x2(o[2], o[3])};
+  if (lse && (e & (kLatent - 1)) == 0)
+    lse[(int64_t)qi * kAttHeads + head] = wt > 0.f ? (mx + log2f(wt)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -997,8 +1041,11 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
     e = launch_kernel(sparse_mla_kernel<false>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx,
                       T, L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
   if (e != hipSuccess || p.splits <= 1) return e;
-  return launch_kernel(combine_kernel, dim3(kAttHeads / kCombHeads, (unsigned)queries), dim3(256), 0,
-                       stream, part_o, part_lse, p.splits, out, lse);
+  if (p.splits <= kCombBatch)
+    return launch_kernel(combine_kernel<1>, dim3(32, (unsigned)queries), dim3(256), 0, stream,
+                         part_o, part_lse, p.splits, out, lse);
+  return launch_kernel(combine_kernel<4>, dim3(32 * 4, (unsigned)queries), dim3(256), 0, stream,
+                       part_o, part_lse, p.splits, out, lse);
 }
 
 }  // namespace lcs
