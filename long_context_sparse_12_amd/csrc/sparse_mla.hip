@@ -17,8 +17,9 @@
 //   O^T[512 x 16] += V_tile^T . P^T            (bf16 MFMA 16x16x32, K = 32 rows)
 // The K order inside each P.V MFMA is a fixed permutation of the 32 rows,
 // chosen so that P^T comes straight out of the S^T accumulators.
-// With more than one split, normalised partial outputs and their log-sum-exp
-// are combined by a second kernel.
+// With more than one split, normalised partial outputs (bf16: the final output
+// is bf16 too, and rounding the partials adds at most 2^-9 relative error) and
+// their log-sum-exp (fp32) are combined by a second kernel.
 #include "common.h"
 
 namespace lcs {
@@ -330,7 +331,7 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv,
     const float* __restrict__ kv_scale, const int32_t* __restrict__ idx, int T, int L, int k,
     int rows_per_split, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   using C = AttnCtx<FP8>;
   __shared__ __attribute__((aligned(16))) uint8_t s_st0[C::kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_st1[C::kStageBytes];
@@ -423,31 +424,26 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
   const int h = c.lane >> 5;
   const int head = 32 * c.hg + (c.lane & 31);
   const float lse2 = l_tot > 0.f ? c.m_run + log2f(l_tot) : -INFINITY;  // log2 domain
-  // lane holds dims 128dq + 32mt + 8(i/4) + 4h + (i&3) of its head
-  if (splits == 1) {
-    uint16_t* orow = out + ((int64_t)qi * kAttHeads + head) * kLatent + 128 * c.dq + 4 * h;
+  // lane holds dims 128dq + 32mt + 8(i/4) + 4h + (i&3) of its head; the
+  // normalised output goes to `out` (one split) or to this split's partial
+  // output (bf16, same layout), whose log-sum-exp the combine needs
+  uint16_t* orow = (splits == 1 ? out + ((int64_t)qi * kAttHeads + head) * kLatent
+                                : part_o + (((int64_t)qi * splits + sp) * kAttHeads + head) * kLatent) +
+                   128 * c.dq + 4 * h;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const v16f& a = c.acc[mt];
-        const uint32_t lo = pack_bf16x2(a[4 * i4] * inv, a[4 * i4 + 1] * inv);
-        const uint32_t hi = pack_bf16x2(a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv);
-        *(v2i*)(orow + 32 * mt + 8 * i4) = v2i{(int)lo, (int)hi};
-      }
-    if (lse && c.dq == 0 && h == 0) lse[(int64_t)qi * kAttHeads + head] = lse2 * kLn2;
-  } else {
-    float* prow = part_o + (((int64_t)qi * splits + sp) * kAttHeads + head) * kLatent + 128 * c.dq +
-                  4 * h;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const v16f& a = c.acc[mt];
-        *(v4f*)(prow + 32 * mt + 8 * i4) =
-            v4f{a[4 * i4] * inv, a[4 * i4 + 1] * inv, a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv};
-      }
-    if (c.dq == 0 && h == 0) part_lse[((int64_t)qi * splits + sp) * kAttHeads + head] = lse2;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const v16f& a = c.acc[mt];
+      const uint32_t lo = pack_bf16x2(a[4 * i4] * inv, a[4 * i4 + 1] * inv);
+      const uint32_t hi = pack_bf16x2(a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv);
+      *(v2i*)(orow + 32 * mt + 8 * i4) = v2i{(int)lo, (int)hi};
+    }
+  if (c.dq == 0 && h == 0) {
+    if (splits > 1)
+      part_lse[((int64_t)qi * splits + sp) * kAttHeads + head] = lse2;
+    else if (lse)
+      lse[(int64_t)qi * kAttHeads + head] = lse2 * kLn2;
   }
 }
 
@@ -752,7 +748,7 @@ __device__ __forceinline__ void s_step(const AttnB& c, SWave& w, int j) {
 __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv, const int32_t* __restrict__ idx,
     int T, int L, int k, int rows_per_split, float sm_scale, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint8_t s_st0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_st1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_st2[kTileBytes];
@@ -886,31 +882,26 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int head = 32 * c.hg + ln;
   const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;  // log2 domain
-  // lane holds dims 256dh + 32mt + 8(i/4) + 4h + (i&3) of its head
-  if (splits == 1) {
-    uint16_t* orow = out + ((int64_t)qi * kAttHeads + head) * kLatent + 256 * w.dh + 4 * h;
+  // lane holds dims 256dh + 32mt + 8(i/4) + 4h + (i&3) of its head; the
+  // normalised output goes to `out` (one split) or to this split's partial
+  // output (bf16, same layout)
+  uint16_t* orow = (splits == 1 ? out + ((int64_t)qi * kAttHeads + head) * kLatent
+                                : part_o + (((int64_t)qi * splits + sp) * kAttHeads + head) * kLatent) +
+                   256 * w.dh + 4 * h;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const v16f& a = w.acc[mt];
-        const uint32_t lo = pack_bf16x2(a[4 * i4] * inv, a[4 * i4 + 1] * inv);
-        const uint32_t hi = pack_bf16x2(a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv);
-        *(v2i*)(orow + 32 * mt + 8 * i4) = v2i{(int)lo, (int)hi};
-      }
-    if (lse && w.dh == 0 && h == 0) lse[(int64_t)qi * kAttHeads + head] = lse2 * kLn2;
-  } else {
-    float* prow = part_o + (((int64_t)qi * splits + sp) * kAttHeads + head) * kLatent + 256 * w.dh +
-                  4 * h;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const v16f& a = w.acc[mt];
-        *(v4f*)(prow + 32 * mt + 8 * i4) =
-            v4f{a[4 * i4] * inv, a[4 * i4 + 1] * inv, a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv};
-      }
-    if (w.dh == 0 && h == 0) part_lse[((int64_t)qi * splits + sp) * kAttHeads + head] = lse2;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const v16f& a = w.acc[mt];
+      const uint32_t lo = pack_bf16x2(a[4 * i4] * inv, a[4 * i4 + 1] * inv);
+      const uint32_t hi = pack_bf16x2(a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv);
+      *(v2i*)(orow + 32 * mt + 8 * i4) = v2i{(int)lo, (int)hi};
+    }
+  if (w.dh == 0 && h == 0) {
+    if (splits > 1)
+      part_lse[((int64_t)qi * splits + sp) * kAttHeads + head] = lse2;
+    else if (lse)
+      lse[(int64_t)qi * kAttHeads + head] = lse2 * kLn2;
   }
 }
 
@@ -924,7 +915,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
 // splits in one memory latency per thread, G = 4 up to 32.
 constexpr int kCombBatch = 8;
 template <int G>
-__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ part_o,
+__global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
                                                       int splits, uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
@@ -936,7 +927,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const int64_t per_split = (int64_t)kAttHeads * kLatent;
   const int e = blockIdx.x * (4 * kCols) + 4 * col;  // element within a split's output
   const int head = e / kLatent;
-  const float* base = part_o + (int64_t)qi * splits * per_split + e;
+  const uint16_t* base = part_o + (int64_t)qi * splits * per_split + e;
   const float* lbase = part_lse + (int64_t)qi * splits * kAttHeads + head;
   float m = -INFINITY, wsum = 0.f;
   v4f acc = {0.f, 0.f, 0.f, 0.f};
@@ -951,7 +942,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
       if (j < nb) {
         const int64_t sp = s0 + G * j;
         l[j] = lbase[sp * kAttHeads];
-        o[j] = *(const v4f*)(base + sp * per_split);
+        const v2i x = *(const v2i*)(base + sp * per_split);  // four bf16
+        o[j] = v4f{__uint_as_float((uint32_t)x[0] << 16), __uint_as_float((uint32_t)x[0] & 0xFFFF0000u),
+                   __uint_as_float((uint32_t)x[1] << 16), __uint_as_float((uint32_t)x[1] & 0xFFFF0000u)};
       }
     }
     float m_new = m;
@@ -1010,7 +1003,7 @@ size_t attn_workspace_bytes(int64_t queries, int k) {
   const SplitPlan pb = plan_splits_b(queries, k);
   const int splits = pa.splits > pb.splits ? pa.splits : pb.splits;
   if (splits <= 1) return 0;
-  size_t o = (size_t)queries * splits * kAttHeads * kLatent * sizeof(float);
+  size_t o = (size_t)queries * splits * kAttHeads * kLatent * sizeof(uint16_t);
   size_t l = (size_t)queries * splits * kAttHeads * sizeof(float);
   return o + l;
 }
@@ -1023,11 +1016,11 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
   // the split-role kernel addresses a sequence's rows with 32-bit offsets
   const bool role_kernel = !kv_fp8 && (int64_t)L * kRowBytes < ((int64_t)1 << 32);
   const SplitPlan p = role_kernel ? plan_splits_b(queries, k) : plan_splits(queries, k);
-  float* part_o = nullptr;
+  uint16_t* part_o = nullptr;
   float* part_lse = nullptr;
   if (p.splits > 1) {
-    part_o = (float*)workspace;
-    part_lse = part_o + (size_t)queries * p.splits * kAttHeads * kLatent;
+    part_o = (uint16_t*)workspace;
+    part_lse = (float*)(part_o + (size_t)queries * p.splits * kAttHeads * kLatent);
   }
   dim3 grid((unsigned)p.splits, (unsigned)queries);
   hipError_t e;
