@@ -426,10 +426,20 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
   const float lse2 = l_tot > 0.f ? c.m_run + log2f(l_tot) : -INFINITY;  // log2 domain
   // lane holds dims 128dq + 32mt + 8(i/4) + 4h + (i&3) of its head; the
   // normalised output goes to `out` (one split) or to this split's partial
-  // output (bf16, same layout), whose log-sum-exp the combine needs
-  uint16_t* orow = (splits == 1 ? out + ((int64_t)qi * kAttHeads + head) * kLatent
-                                : part_o + (((int64_t)qi * splits + sp) * kAttHeads + head) * kLatent) +
-                   128 * c.dq + 4 * h;
+  // output (bf16, same layout), whose log-sum-exp the combine needs. As in
+  // the split-role kernel below, each wave transposes its [32 heads][128
+  // dims] block through LDS (rows 272 bytes apart; with FP8 rows two waves
+  // per stage buffer and the last two in the conversion buffer, with bf16
+  // rows four per stage buffer) and stores whole 256-byte rows, four per
+  // instruction.
+  constexpr int kEpiRow = 272, kEpiWave = 32 * kEpiRow;
+  static_assert(2 * kEpiWave <= C::kStageBytes && 4 * kEpiWave <= kTileBytes, "epilogue staging");
+  __syncthreads();  // every wave is done with the stage and conversion buffers
+  // (constant indices into c.st: a runtime index would put the context in scratch)
+  const int eslot = FP8 ? c.wave >> 1 : c.wave >> 2;
+  uint8_t* ebuf = eslot == 0 ? c.st[0] : eslot == 1 ? c.st[1] : eslot == 2 ? c.st[2] : c.cvt;
+  uint8_t* eb = ebuf + (FP8 ? (c.wave & 1) : (c.wave & 3)) * kEpiWave;
+  const int ln = c.lane & 31;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -437,8 +447,17 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
       const v16f& a = c.acc[mt];
       const uint32_t lo = pack_bf16x2(a[4 * i4] * inv, a[4 * i4 + 1] * inv);
       const uint32_t hi = pack_bf16x2(a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv);
-      *(v2i*)(orow + 32 * mt + 8 * i4) = v2i{(int)lo, (int)hi};
+      *(v2i*)(eb + ln * kEpiRow + 2 * (32 * mt + 8 * i4 + 4 * h)) = v2i{(int)lo, (int)hi};
     }
+  uint16_t* obase = (splits == 1 ? out + ((int64_t)qi * kAttHeads + 32 * c.hg) * kLatent
+                                 : part_o + (((int64_t)qi * splits + sp) * kAttHeads + 32 * c.hg) * kLatent) +
+                    128 * c.dq;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int hl = 4 * it + (c.lane >> 4);  // head within the group
+    const v4i x = *(const v4i*)(eb + hl * kEpiRow + 16 * (c.lane & 15));
+    *(v4i*)(obase + hl * kLatent + 8 * (c.lane & 15)) = x;
+  }
   if (c.dq == 0 && h == 0) {
     if (splits > 1)
       part_lse[((int64_t)qi * splits + sp) * kAttHeads + head] = lse2;
@@ -882,12 +901,17 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int head = 32 * c.hg + ln;
   const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;  // log2 domain
-  // lane holds dims 256dh + 32mt + 8(i/4) + 4h + (i&3) of its head; the
+  // lane holds dims 256dh + 32mt + 8(i/4) + 4h + (i&3) of its head. The
   // normalised output goes to `out` (one split) or to this split's partial
-  // output (bf16, same layout)
-  uint16_t* orow = (splits == 1 ? out + ((int64_t)qi * kAttHeads + head) * kLatent
-                                : part_o + (((int64_t)qi * splits + sp) * kAttHeads + head) * kLatent) +
-                   256 * w.dh + 4 * h;
+  // output (bf16, same layout). Stored lane-per-head, a store instruction
+  // would write 16 bytes into each of 32 rows; instead each PV wave first
+  // transposes its [32 heads][256 dims] block through its own stage buffer
+  // (idle now: every gather has landed and been read), rows 528 bytes apart,
+  // and then stores two whole 512-byte rows per instruction. A wave's LDS
+  // accesses complete in order, so it reads back its own writes unsynchronised.
+  constexpr int kEpiRow = 528;
+  static_assert(32 * kEpiRow <= kTileBytes, "epilogue staging");
+  uint8_t* eb = pw == 0 ? c.st[0] : pw == 1 ? c.st[1] : pw == 2 ? c.st[2] : c.st[3];  // not c.st[pw]: scratch
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -895,8 +919,17 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
       const v16f& a = w.acc[mt];
       const uint32_t lo = pack_bf16x2(a[4 * i4] * inv, a[4 * i4 + 1] * inv);
       const uint32_t hi = pack_bf16x2(a[4 * i4 + 2] * inv, a[4 * i4 + 3] * inv);
-      *(v2i*)(orow + 32 * mt + 8 * i4) = v2i{(int)lo, (int)hi};
+      *(v2i*)(eb + ln * kEpiRow + 2 * (32 * mt + 8 * i4 + 4 * h)) = v2i{(int)lo, (int)hi};
     }
+  uint16_t* obase = (splits == 1 ? out + ((int64_t)qi * kAttHeads + 32 * c.hg) * kLatent
+                                 : part_o + (((int64_t)qi * splits + sp) * kAttHeads + 32 * c.hg) * kLatent) +
+                    256 * w.dh;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int hl = 2 * it + h;  // head within the group
+    const v4i x = *(const v4i*)(eb + hl * kEpiRow + 16 * ln);
+    *(v4i*)(obase + hl * kLatent + 8 * ln) = x;
+  }
   if (w.dh == 0 && h == 0) {
     if (splits > 1)
       part_lse[((int64_t)qi * splits + sp) * kAttHeads + head] = lse2;
