@@ -499,7 +499,7 @@ __device__ __forceinline__ Role role_of(int wave) {
 #define LCS_ATTN_B_TARGET_WGS 256
 #endif
 #ifndef LCS_ATTN_B_MAX_SPLITS
-#define LCS_ATTN_B_MAX_SPLITS 64
+#define LCS_ATTN_B_MAX_SPLITS 16  // fewer, longer splits pipeline better than a wider combine
 #endif
 
 __host__ __device__ inline SplitPlan plan_splits_b(int64_t queries, int k) {
@@ -526,6 +526,11 @@ __host__ __device__ inline SplitPlan plan_splits_b(int64_t queries, int k) {
 // conflicts (row 8 apart: swz_b(r + 8) = swz_b(r) ^ 2; 16 apart: equal).
 __device__ __forceinline__ int swz_b(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
+// byte offset of bf16 granule cg (8 dims) of row r in a stage
+__device__ __forceinline__ int stage_off_b(int r, int cg) {
+  return r * kRowBytes + 16 * ((cg & ~7) | ((cg & 7) ^ swz_b(r)));
+}
+
 // state shared by both roles
 struct AttnB {
   uint8_t* st[kStagesB];
@@ -533,6 +538,8 @@ struct AttnB {
   float* alpha;     // [2 parity][2 hg][32 heads]
   int* flag;        // [2 parity][2 hg]
   int32_t* ring;    // [4 slots][32 rows]  positions of the tiles t with t & 3 = slot
+  float* sring;     // [4 slots][32 rows]  FP8 row scales of the same tiles
+  const float* kscale;   // FP8 row scales of this sequence (kv_scale + b * L)
   const int32_t* idx_q;  // this split's selected positions (global memory)
   int n_rows, n_tiles;
   int wave, lane, hg;
@@ -561,11 +568,22 @@ __device__ __forceinline__ void ring_put(const AttnB& c, int tile, int32_t p) {
   if (c.lane < kTileRows) pos_slot(c, tile)[c.lane] = r < c.n_rows ? p : -1;
 }
 
+// FP8 KV: the row scales follow the positions one step later (their loads
+// need the positions): tile t's scales go into slot t & 3 of the scale ring
+// in step t-3 and are read by the S waves in step t-1.
+__device__ __forceinline__ float load_scale(const AttnB& c, int32_t p) {
+  return c.kscale[p >= 0 ? p : 0];
+}
+__device__ __forceinline__ void scale_put(const AttnB& c, int tile, float v) {
+  if (c.lane < kTileRows) c.sring[(tile & (kPosSlots - 1)) * kTileRows + c.lane] = v;
+}
+
 struct SWave {
   v8bf qT[36];  // Q^T: head 32hg + (lane&31), dims 16ks + 8(lane>>5) .. +8
   float c_log;
   float m_run, l_run;
   int32_t pn;  // S wave 0: positions of the next tile to enter the ring
+  float sn;    // S wave 0, FP8: scales of the next tile to enter the scale ring
 };
 
 struct PWave {
@@ -575,10 +593,65 @@ struct PWave {
 
 struct GWave {
   int g;                // 0 or 1 (wave-uniform)
-  const uint8_t* kvb;   // this sequence's rows: kv + b * L * 1152
+  const uint8_t* kvb;   // this sequence's rows: kv + b * L * (1152 or 576)
   int dma_row[kDmaPerB];  // row inside the tile of each gather
   int dma_off[kDmaPerB];  // byte offset inside the row (swizzled granule)
 };
+
+// FP8 KV: a tile is 32 rows x 36 granules of 16 E4M3 codes. Gather lane (g, l)
+// carries granules 64 (g + 2 i) + l, i < 9: it loads them into registers one
+// step ahead, then widens each to two bf16 granules (exact) and writes them
+// into the stage in the bf16 kernel's swizzled layout. These waves issue only
+// register loads, a fixed nine per step, so the compiler's own waits before
+// the widening leave the next tile's loads in flight.
+constexpr int kFp8Per = kTileRows * (kKvDim / 16) / (64 * kGatherWaves);  // 9
+struct GWave8 {
+  int g;
+  const uint8_t* kvb;     // kv + b * L * 576
+  int row[kFp8Per];       // tile row of each granule
+  int src[kFp8Per];       // byte offset inside the 576-byte row
+  int dst[kFp8Per];       // stage byte offset of its first bf16 granule
+  int dst2[kFp8Per];      // ... and of its second
+  v4i fr[2][kFp8Per];     // loaded codes, by tile parity
+};
+
+__device__ __forceinline__ int stage_off_b(int r, int cg);
+
+template <int B>
+__device__ __forceinline__ void fetch_fp8(const AttnB& c, GWave8& w, int tile) {
+  const int32_t* slot = pos_slot(c, tile);
+  int32_t rows[kFp8Per];
+#pragma unroll
+  for (int i = 0; i < kFp8Per; ++i) rows[i] = slot[w.row[i]];
+#pragma unroll
+  for (int i = 0; i < kFp8Per; ++i) {
+    const uint32_t s = rows[i] >= 0 ? (uint32_t)rows[i] : 0u;  // padding rows load row 0 (masked)
+    // 32-bit offset from the sequence base (the launcher keeps L * 576 < 2^32)
+    w.fr[B][i] = *(const v4i*)(w.kvb + (s * (uint32_t)kKvDim + (uint32_t)w.src[i]));
+  }
+}
+
+__device__ __forceinline__ int widen2(v2f f) {
+  return (int)((__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u));
+}
+
+template <int S, int B>
+__device__ __forceinline__ void store_fp8(const AttnB& c, const GWave8& w) {
+#pragma unroll
+  for (int i = 0; i < kFp8Per; ++i) {
+    const v4i x = w.fr[B][i];
+    const v4i lo = v4i{widen2(__builtin_amdgcn_cvt_pk_f32_fp8(x[0], false)),
+                       widen2(__builtin_amdgcn_cvt_pk_f32_fp8(x[0], true)),
+                       widen2(__builtin_amdgcn_cvt_pk_f32_fp8(x[1], false)),
+                       widen2(__builtin_amdgcn_cvt_pk_f32_fp8(x[1], true))};
+    const v4i hi = v4i{widen2(__builtin_amdgcn_cvt_pk_f32_fp8(x[2], false)),
+                       widen2(__builtin_amdgcn_cvt_pk_f32_fp8(x[2], true)),
+                       widen2(__builtin_amdgcn_cvt_pk_f32_fp8(x[3], false)),
+                       widen2(__builtin_amdgcn_cvt_pk_f32_fp8(x[3], true))};
+    *(v4i*)(c.st[S] + w.dst[i]) = lo;
+    *(v4i*)(c.st[S] + w.dst2[i]) = hi;
+  }
+}
 
 // gathers of `tile` into stage S: gather-wave lane (g, l), gather i covers
 // LDS bytes [1024 (g + 2 i), +1024) of the stage, 16 bytes per lane
@@ -598,7 +671,7 @@ __device__ __forceinline__ void issue_tile_b(const AttnB& c, const GWave& w, int
 
 // S^T of one tile and its softmax (S waves); P^T, alpha and the rescale flag
 // go to parity buffer `par`
-template <int S>
+template <int S, bool FP8>
 __device__ __forceinline__ void s_phase(const AttnB& c, SWave& w, int tile, int par) {
   const int lane = c.lane, ln = lane & 31, h = lane >> 5;
   const uint8_t* tb = c.st[S];
@@ -634,9 +707,23 @@ __device__ __forceinline__ void s_phase(const AttnB& c, SWave& w, int tile, int 
   const uint32_t valid = (uint32_t)__ballot(pos_slot(c, tile)[ln] >= 0);
   // lane holds head 32hg + (lane&31) for rows 8(i/4) + 4h + (i&3); raw dot
   // products here, the scale enters through the exponent's FMA below
+  // FP8: dequantisation scales of this lane's 16 rows 8(i/4) + 4h + (i&3)
+  // (read after the MFMAs, so that they hold no registers during them)
+  float psc[16];
+  if (FP8) {
+    const float* sc = c.sring + (tile & (kPosSlots - 1)) * kTileRows + 4 * h;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const v4f v = *(const v4f*)(sc + 8 * q4);
+      psc[4 * q4] = v[0];
+      psc[4 * q4 + 1] = v[1];
+      psc[4 * q4 + 2] = v[2];
+      psc[4 * q4 + 3] = v[3];
+    }
+  }
   float t[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) t[i] = se[i] + so[i];
+  for (int i = 0; i < 16; ++i) t[i] = FP8 ? (se[i] + so[i]) * psc[i] : se[i] + so[i];
   const bool all_valid = valid == 0xFFFFFFFFu;
   if (!all_valid) {
     const uint32_t mine = valid >> (4 * h);
@@ -681,6 +768,12 @@ __device__ __forceinline__ void s_phase(const AttnB& c, SWave& w, int tile, int 
   w.m_run = m_new;
   if (lane == 0) c.flag[par * 2 + c.hg] = rescale ? 1 : 0;
   uint8_t* pb = c.p_buf + ((par * 2 + c.hg) * 64 + lane) * 32;
+  // FP8: the stage holds the unscaled codes (widened), so each row's scale
+  // also weights its P entry: sum_r p_r (code_r * scale_r) = sum_r (p_r scale_r) code_r
+  if (FP8) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] *= psc[i];
+  }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int o = 8 * ks;
@@ -750,24 +843,53 @@ __device__ __forceinline__ void g_step(const AttnB& c, const GWave& w, int j) {
   lds_barrier();
 }
 
+// FP8 gather side of pipeline step j: load tile j+3's codes (positions from
+// the ring slot written in step j-1), then widen tile j+2's (loaded in step
+// j-1) into stage (SJ+2)%4, which held tile j-2, finished before this step.
+// Every step loads and widens, past the split's end too (valid addresses;
+// the stage is not read again): loads whose only use sat under a branch
+// would be moved into it by the compiler, next to the widening. For the same
+// reason the gather waves run their steps in groups of four without a
+// branch; a step past the last tile (j >= n_tiles) skips only the barrier,
+// which the other roles do not have for it (they are done with every stage
+// by then, and the final barrier orders these writes before the epilogue's).
+template <int SJ>
+__device__ __forceinline__ void g_step8(const AttnB& c, GWave8& w, int j) {
+  fetch_fp8<(SJ + 3) & 1>(c, w, j + 3);
+  __builtin_amdgcn_sched_barrier(0);  // the loads go out before the widening
+  store_fp8<(SJ + 2) % kStagesB, SJ & 1>(c, w);
+  if (j < c.n_tiles) lds_barrier();
+}
+
 // S side of pipeline step j: S wave 0 puts tile j+4's positions (loaded one
 // step earlier) into the ring slot of tile j (read for the last time in step
-// j-1) and loads tile j+5's; then score tile j+1 (stage (SJ+1)%4). The gather
-// waves read tile j+4's slot in step j+1, after this step's barrier.
-template <int SJ>
+// j-1) and loads tile j+5's; with FP8 KV it also puts tile j+3's row scales
+// (loaded one step earlier) into the scale ring and loads tile j+4's. Then
+// score tile j+1 (stage (SJ+1)%4). The gather waves read tile j+4's slot in
+// step j+1, after this step's barrier.
+template <int SJ, bool FP8>
 __device__ __forceinline__ void s_step(const AttnB& c, SWave& w, int j) {
   if (c.wave == 0) {
     ring_put(c, j + 4, w.pn);
+    if (FP8) {
+      scale_put(c, j + 3, w.sn);
+      w.sn = load_scale(c, w.pn);
+    }
     w.pn = load_pos(c, j + 5);
   }
-  if (j + 1 < c.n_tiles) s_phase<(SJ + 1) % kStagesB>(c, w, j + 1, (j + 1) & 1);
+  if (j + 1 < c.n_tiles) s_phase<(SJ + 1) % kStagesB, FP8>(c, w, j + 1, (j + 1) & 1);
   lds_barrier();
 }
 
+// (kv without __restrict__: the FP8 gathers load it into registers, and a
+// restrict-qualified load may be moved across the barriers' memory clobbers,
+// away from the step that is meant to issue it)
+template <bool FP8>
 __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
-    const uint16_t* __restrict__ q, const void* __restrict__ kv, const int32_t* __restrict__ idx,
-    int T, int L, int k, int rows_per_split, float sm_scale, uint16_t* __restrict__ out,
-    float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
+    const uint16_t* __restrict__ q, const void* kv, const float* __restrict__ kv_scale,
+    const int32_t* __restrict__ idx, int T, int L, int k, int rows_per_split, float sm_scale,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
+    float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint8_t s_st0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_st1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_st2[kTileBytes];
@@ -776,6 +898,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   __shared__ float s_alpha[2 * 2 * 32];
   __shared__ int s_flag[2 * 2];
   __shared__ int32_t s_ring[kPosSlots * kTileRows];
+  __shared__ __attribute__((aligned(16))) float s_sring[FP8 ? kPosSlots * kTileRows : 4];
   __shared__ float s_ml[2 * 2 * 32];
 
   const int qi = blockIdx.y;  // flattened (b, t)
@@ -793,6 +916,8 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   c.alpha = s_alpha;
   c.flag = s_flag;
   c.ring = s_ring;
+  c.sring = s_sring;
+  c.kscale = FP8 ? kv_scale + (int64_t)b * L : nullptr;
   c.lane = tid & 63;
   c.wave = tid >> 6;
   const Role role = role_of(c.wave);
@@ -817,9 +942,12 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
                          8 * (c.lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) w.qT[ks] = as_v8bf(*(const v4i*)(qh + 16 * ks));
+    int32_t p0 = 0, p1 = 0, p2 = 0;
     if (c.wave == 0) {
       // tiles 0..2 into the ring before the gathers start; tile 3 goes in at step -1
-      const int32_t p0 = load_pos(c, 0), p1 = load_pos(c, 1), p2 = load_pos(c, 2);
+      p0 = load_pos(c, 0);
+      p1 = load_pos(c, 1);
+      p2 = load_pos(c, 2);
       w.pn = load_pos(c, 3);
       ring_put(c, 0, p0);
       ring_put(c, 1, p1);
@@ -827,13 +955,21 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
     }
     wait_vm<0>();
     __syncthreads();
+    if (FP8 && c.wave == 0) {
+      // scales of tiles 0 and 1 (they need the positions) land while the
+      // gather waves fetch tile 0; tile 2's go in at step -1
+      const float s0 = load_scale(c, p0), s1 = load_scale(c, p1);
+      w.sn = load_scale(c, p2);
+      scale_put(c, 0, s0);
+      scale_put(c, 1, s1);
+    }
     lds_barrier();  // prologue (tile 0 landed)
-    s_step<3>(c, w, -1);  // scores tile 0 from stage 0
+    s_step<3, FP8>(c, w, -1);  // scores tile 0 from stage 0
     for (int j = 0; j < c.n_tiles; j += kStagesB) {
-      s_step<0>(c, w, j);
-      if (j + 1 < c.n_tiles) s_step<1>(c, w, j + 1);
-      if (j + 2 < c.n_tiles) s_step<2>(c, w, j + 2);
-      if (j + 3 < c.n_tiles) s_step<3>(c, w, j + 3);
+      s_step<0, FP8>(c, w, j);
+      if (j + 1 < c.n_tiles) s_step<1, FP8>(c, w, j + 1);
+      if (j + 2 < c.n_tiles) s_step<2, FP8>(c, w, j + 2);
+      if (j + 3 < c.n_tiles) s_step<3, FP8>(c, w, j + 3);
     }
     // publish each head's exponent offset and sum
     float l_tot = w.l_run;
@@ -845,7 +981,38 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
     __syncthreads();
     return;
   }
-  if (role == kRoleGather) {
+  if (FP8 && role == kRoleGather) {
+    GWave8 w;
+    w.g = __builtin_amdgcn_readfirstlane(c.wave - 4);
+    w.kvb = (const uint8_t*)kv + (int64_t)b * L * kKvDim;
+#pragma unroll
+    for (int i = 0; i < kFp8Per; ++i) {
+      const int gi = 64 * (w.g + kGatherWaves * i) + c.lane;  // FP8 granule of the tile
+      const int r = gi / (kKvDim / 16), c8 = gi - r * (kKvDim / 16);
+      w.row[i] = r;
+      w.src[i] = 16 * c8;
+      w.dst[i] = stage_off_b(r, 2 * c8);
+      w.dst2[i] = stage_off_b(r, 2 * c8 + 1);
+    }
+    __syncthreads();
+    // prologue: tiles 0 and 1 loaded, tile 0 widened into stage 0
+    fetch_fp8<0>(c, w, 0);
+    fetch_fp8<1>(c, w, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_fp8<0, 0>(c, w);
+    lds_barrier();
+    g_step8<3>(c, w, -1);  // loads tile 2, widens tile 1 into stage 1
+    for (int j = 0; j < c.n_tiles; j += kStagesB) {
+      g_step8<0>(c, w, j);
+      g_step8<1>(c, w, j + 1);
+      g_step8<2>(c, w, j + 2);
+      g_step8<3>(c, w, j + 3);
+    }
+    wait_vm<0>();  // loads past the split's end are still in flight
+    __syncthreads();
+    return;
+  }
+  if (!FP8 && role == kRoleGather) {
     GWave w;
     w.g = __builtin_amdgcn_readfirstlane(c.wave - 4);
     w.kvb = (const uint8_t*)kv + (int64_t)b * L * kRowBytes;
@@ -1047,7 +1214,7 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
                              void* workspace, hipStream_t stream) {
   const int64_t queries = (int64_t)B * T;
   // the split-role kernel addresses a sequence's rows with 32-bit offsets
-  const bool role_kernel = !kv_fp8 && (int64_t)L * kRowBytes < ((int64_t)1 << 32);
+  const bool role_kernel = (int64_t)L * (kv_fp8 ? kKvDim : kRowBytes) < ((int64_t)1 << 32);
   const SplitPlan p = role_kernel ? plan_splits_b(queries, k) : plan_splits(queries, k);
   uint16_t* part_o = nullptr;
   float* part_lse = nullptr;
@@ -1057,12 +1224,16 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
   }
   dim3 grid((unsigned)p.splits, (unsigned)queries);
   hipError_t e;
-  if (kv_fp8)
+  if (role_kernel && kv_fp8)
+    e = launch_kernel(sparse_mla_b_kernel<true>, grid, dim3(kThreadsB), 0, stream, q, kv, kv_scale,
+                      idx, T, L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
+  else if (role_kernel)
+    e = launch_kernel(sparse_mla_b_kernel<false>, grid, dim3(kThreadsB), 0, stream, q, kv,
+                      (const float*)nullptr, idx, T, L, k, p.rows_per_split, sm_scale, out, lse,
+                      part_o, part_lse);
+  else if (kv_fp8)
     e = launch_kernel(sparse_mla_kernel<true>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx, T,
                       L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
-  else if (role_kernel)
-    e = launch_kernel(sparse_mla_b_kernel, grid, dim3(kThreadsB), 0, stream, q, kv, idx, T, L, k,
-                      p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
   else
     e = launch_kernel(sparse_mla_kernel<false>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx,
                       T, L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
