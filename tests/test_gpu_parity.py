@@ -227,6 +227,42 @@ def test_sparse_mla_empty_selection():
     assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
 
 
+@pytest.mark.parametrize("fp8", [True, False], ids=["fp8", "bf16"])
+def test_sparse_mla_rows_past_32bit_offsets(fp8):
+    """A sequence whose KV rows reach past 2^32 bytes (4.3 GB of KV for one
+    sequence): the launcher then takes the 64-bit-addressed split-dims kernel.
+    Positions spread over the whole range, the last eight rows included; the
+    oracle runs on the gathered rows only (host-generated at those positions)."""
+    row_bytes = 576 if fp8 else 1152
+    L = (1 << 32) // row_bytes + 4096
+    B, T, k = 1, 2, 2048
+    _say("case: sparse_mla rows past 2^32 bytes, fp8=%d L=%d" % (fp8, L))
+    w = wl.Workload("attn-long-rows", seed=11, B=B, T=T, L=L, n_layers=1, kv_fp8=fp8)
+    kv, sc = wl.dev_kv(w, 0, DEV)
+    q = wl.host_attn_q(w, 0)
+    rs = np.random.default_rng(7)
+    idx = np.empty((B, T, k), np.int32)
+    for t in range(T):
+        pos = np.unique(rs.integers(0, L - 8, size=3 * k))[: k - 8]
+        pos = np.concatenate([pos, np.arange(L - 8, L)])
+        assert len(pos) == k and pos[-1] * row_bytes >= (1 << 32)
+        idx[0, t] = np.sort(rs.permutation(pos))
+    out = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+    ws = _zeros(lcs.attn_workspace_bytes(B, T, k))
+    lcs.sparse_mla_attn(to_dev(q), kv, sc, to_dev(idx), 1 / 24, out, lse, ws)
+    torch.cuda.synchronize()
+    del kv, sc
+    torch.cuda.empty_cache()
+    for t in range(T):
+        kv_s, sc_s = wl.host_kv_rows(w, 0, 0, idx[0, t])
+        idx_s = np.arange(k, dtype=np.int32).reshape(1, 1, k)
+        _, ref_lse, ref64 = oracle.sparse_mla(q[:, t:t + 1], kv_s, sc_s, idx_s, 1 / 24, want64=True)
+        mx, ratio, lerr = check_attention(out[:, t:t + 1], ref64, lse[:, t:t + 1],
+                                          ref_lse.astype(np.float64))
+        _say("  t=%d max-abs %.3g, lse err %.3g" % (t, mx, lerr))
+
+
 # ------------------------------------------------------------------ composite
 def _dev_layers(layers):
     out = []
