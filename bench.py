@@ -27,6 +27,7 @@ METRIC = ("decode tokens/s/GPU at L=128K & 1M (indexer+top-k+sparse attn); % HBM
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
 IDX_BYTES_PER_KEY = 132  # 128 E4M3 codes + fp32 scale
+IDX_PREFILL_MIN_T = 16  # T at which idx_score switches to the dense FP8-MFMA kernel
 IDX_BYTES_PER_QUERY = 32 * 128 + 32 * 4 + 32 * 4  # q8, q_scale, w
 ATT_BYTES_PER_QUERY_IO = 64 * 576 * 2 + 64 * 512 * 2 + 64 * 4  # q, out, lse
 ROTATIONS = 3  # query sets cycled between steps so no step reuses another's gathers
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode128k",
-                    choices=["tiny", "decode128k", "prefill", "decode1m", "mtp1m"])
+                    choices=["tiny", "decode128k", "prefill", "decode1m", "mtp1m", "verify128k"])
     ap.add_argument("--cpu-rows", type=int, default=None, help="sequences in the oracle sample")
     ap.add_argument("--cpu-layers", type=int, default=None, help="layers in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -281,7 +282,9 @@ def main():
     sb = step_bytes(w, False)
     res = {
         "metric": METRIC, "value": round(value, 1),
-        "unit": "draft tokens/s" if w.mtp_steps else ("prefill tokens/s" if w.T > 4 else "tokens/s"),
+        "unit": ("draft tokens/s" if w.mtp_steps else
+                 "prefill tokens/s" if w.T >= IDX_PREFILL_MIN_T else
+                 "verified tokens/s" if w.prefix >= 0 else "tokens/s"),
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8+bf16 (fp32 accumulate)", "data": "synthetic",
@@ -298,7 +301,7 @@ def main():
         sha = _sha(os.path.join(ROOT, "long_context_sparse_12_amd", "csrc", "idx_score.hip"))
         tr = TRAFFIC.get(w.name)
         traffic = tr["bytes"] if tr and tr["sha"] == sha else None
-        if w.T > 4:
+        if w.T >= IDX_PREFILL_MIN_T:
             # dense FP8 contraction: 32 heads x 128 dims = 4096 MACs = 8192 FLOP per
             # visible (t, s) pair
             flops = 8192.0 * float(w.vis_len().astype("int64").sum())

@@ -74,6 +74,10 @@ WORKLOADS = {
     # MTP draft reuse, 7 draft steps on one shared layer
     "mtp1m": Workload("mtp-B8-L1048576-7steps-fp8kv", seed=5, B=8, T=1, L=1 << 20, n_layers=7,
                       kv_fp8=True, mtp_steps=7),
+    # MTP verify: 1 + 5 draft tokens per sequence scored in one pass, causal
+    # among themselves (vis_len = L - 6 + t + 1), one 4-layer group
+    "verify128k": Workload("verify-B32-T6-L131072-group4", seed=6, B=32, T=6, L=131072,
+                           n_layers=4, plant_permyriad=100, prefix=131072 - 6),
 }
 
 

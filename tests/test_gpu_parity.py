@@ -372,6 +372,17 @@ def test_mtp_draft_reuse_small():
         assert torch.equal(ly["out"], layers_d2[0]["out"])
 
 
+def test_verify_multi_token_small():
+    """MTP verify / multi-token decode: 1 + 5 draft tokens per sequence in one
+    pass, causal among themselves, through the whole group."""
+    w = wl.Workload("verify-small", seed=24, B=3, T=6, L=7000, n_layers=4, prefix=7000 - 6,
+                    plant_permyriad=100)
+    _say("case: composite %s" % w.name)
+    layers_h = _host_layers(w, 4, [0])
+    layers_d, idx_out = _run_composite(w, layers_h, lcs.SCHED_GROUP4)
+    _compare_composite(w, layers_h, layers_d, idx_out, lcs.SCHED_GROUP4)
+
+
 def test_prefill_causal_small():
     w = wl.Workload("prefill-small", seed=23, B=1, T=40, L=9000, n_layers=4, prefix=9000 - 40)
     _say("case: composite %s" % w.name)
