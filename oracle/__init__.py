@@ -148,3 +148,50 @@ def indexshare(layers, sched, vis_len, k, sm_scale, kv_fp8=False, mtp_steps=0, m
                                   mtp_steps, 1 if kv_fp8 else 0, vis_len.ctypes.data, B, T, L, k,
                                   float(sm_scale), idx_out.ctypes.data), "indexshare")
     return outs, lses, idx_out
+
+
+_lib.oracle_encode_e4m3.argtypes = [ctypes.c_double]
+_lib.oracle_encode_e4m3.restype = ctypes.c_uint8
+_lib.oracle_quantize_e4m3.argtypes = [_p, ctypes.c_int64, _i32, _p, _p]
+_lib.oracle_quantize_e4m3.restype = ctypes.c_int
+_lib.oracle_cache_append.argtypes = [_p, _p, _i32, _p] + [_i32] * 3 + [_p] * 4
+_lib.oracle_cache_append.restype = ctypes.c_int
+
+
+def encode_e4m3(v):
+    """finite value -> E4M3 code (saturating, nearest, ties to the even code)"""
+    return int(_lib.oracle_encode_e4m3(float(v)))
+
+
+def quantize_e4m3(x_bits):
+    """x_bits [..., D] uint16 bf16 bits -> (codes uint8 [..., D], scales f32 [...])"""
+    x = _c(x_bits, np.uint16)
+    D = x.shape[-1]
+    rows = x.size // D
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty(x.shape[:-1], np.float32)
+    _check(_lib.oracle_quantize_e4m3(x.ctypes.data, rows, D, codes.ctypes.data,
+                                     scales.ctypes.data), "quantize_e4m3")
+    return codes, scales
+
+
+def cache_append(k_new, kv_new, pos, k8, k_scale, kv, kv_scale):
+    """Writes the new tokens into copies of the caches and returns them.
+    k_new [B][T][128] / kv_new [B][T][576] uint16 bf16 bits (either may be
+    None), pos [B][T] int32; k8 [B][L][128] u8, k_scale [B][L] f32,
+    kv [B][L][576] (uint16 bf16 bits, or uint8 codes with kv_scale [B][L]).
+    Returns (k8, k_scale, kv, kv_scale) with None where not given."""
+    pos = _c(pos, np.int32)
+    B, T = pos.shape
+    kn = _c(k_new, np.uint16) if k_new is not None else None
+    vn = _c(kv_new, np.uint16) if kv_new is not None else None
+    k8o = np.array(k8, np.uint8, copy=True) if k8 is not None else None
+    kso = np.array(k_scale, np.float32, copy=True) if k_scale is not None else None
+    fp8 = kv is not None and np.asarray(kv).dtype == np.uint8
+    kvo = np.array(kv, np.uint8 if fp8 else np.uint16, copy=True) if kv is not None else None
+    kvso = np.array(kv_scale, np.float32, copy=True) if kv_scale is not None else None
+    L = (k8o if k8o is not None else kvo).shape[1]
+    ptr = lambda a: a.ctypes.data if a is not None else None  # noqa: E731
+    _check(_lib.oracle_cache_append(ptr(kn), ptr(vn), int(fp8), pos.ctypes.data, B, T, L,
+                                    ptr(k8o), ptr(kso), ptr(kvo), ptr(kvso)), "cache_append")
+    return k8o, kso, kvo, kvso

@@ -67,6 +67,98 @@ uint16_t oracle_round_bf16(double x) {
   return (uint16_t)(sign | (c.u >> 16));
 }
 
+/* double -> E4M3 code. The FP8 release of the model stores E4M3 (the weight
+ * file table under "40B Active，为什么仍要装下 0.465～1.507 TB 权重", ailearn
+ * GLM-5.2 special edition), but no page gives a rounding rule; the reading is saturation to +-448, then the
+ * nearest finite code, ties to the even code (the code whose last mantissa
+ * bit is 0), with the sign kept for zero results. Written as a search over
+ * all 127 finite non-negative codes so that it can be checked by eye. */
+uint8_t oracle_encode_e4m3(double v) {
+  int neg = signbit(v) ? 1 : 0;
+  double a = fabs(v);
+  if (a > 448.0) a = 448.0;
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) { /* values increase strictly with c */
+    double d = fabs(oracle_e4m3((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best_d = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(best | (neg << 7));
+}
+
+/* One row of D bf16 values -> D codes and one fp32 scale. The pages keep the
+ * KV cache in FP8 (the closing line of the training section of "GLM-5.2 — 1M
+ * 上下文开放权重的长程任务旗舰"; the `fp8_ds_mla` cache type in the vLLM launch
+ * of the Hygon DCU forum post) without saying how a row is scaled. Reading:
+ * amax = max |x|, scale = fl32(amax / 448) (1 when amax = 0), and
+ * code_i = encode(fl32(x_i / scale)); the quotient is taken in binary32, so
+ * the code a value gets is decided in binary32. Non-finite values: rejected. */
+static int quantize_row(const uint16_t* x, int32_t D, uint8_t* codes, float* scale_out) {
+  float amax = 0.0f;
+  for (int32_t i = 0; i < D; ++i) {
+    double v = oracle_bf16(x[i]);
+    if (!isfinite(v)) return 1;
+    float a = (float)fabs(v); /* exact: a bf16 value is a binary32 value */
+    if (a > amax) amax = a;
+  }
+  float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int32_t i = 0; i < D; ++i) {
+    float q = (float)oracle_bf16(x[i]) / scale; /* binary32 division */
+    codes[i] = oracle_encode_e4m3((double)q);
+  }
+  *scale_out = scale;
+  return 0;
+}
+
+int oracle_quantize_e4m3(const uint16_t* x, int64_t rows, int32_t D, uint8_t* codes,
+                         float* scales) {
+  if (!x || !codes || !scales || rows < 0 || D <= 0) return 1;
+  for (int64_t r = 0; r < rows; ++r)
+    if (quantize_row(x + r * D, D, codes + r * D, scales + r)) return 1;
+  return 0;
+}
+
+/* New tokens enter the caches at their positions: the indexer key row is
+ * quantised (one scale per key), the latent row is copied (bf16 cache) or
+ * quantised (FP8 cache, one scale per row). Tokens whose position lies
+ * outside [0, L) are not written; two tokens of one sequence with the same
+ * position are rejected. */
+int oracle_cache_append(const uint16_t* k_new, const uint16_t* kv_new, int32_t kv_fp8,
+                        const int32_t* pos, int32_t B, int32_t T, int32_t L,
+                        uint8_t* k8, float* k_scale, void* kv, float* kv_scale) {
+  if (!pos || B <= 0 || T <= 0 || L <= 0 || (!k_new && !kv_new)) return 1;
+  if (k_new && (!k8 || !k_scale)) return 1;
+  if (kv_new && (!kv || (kv_fp8 && !kv_scale))) return 1;
+  unsigned char* seen = calloc((size_t)L, 1);
+  if (!seen) return 1;
+  int rc = 0;
+  for (int32_t b = 0; b < B && !rc; ++b) {
+    memset(seen, 0, (size_t)L);
+    for (int32_t t = 0; t < T && !rc; ++t) {
+      int64_t tok = (int64_t)b * T + t;
+      int32_t p = pos[tok];
+      if (p < 0 || p >= L) continue;
+      if (seen[p]) { rc = 1; break; }
+      seen[p] = 1;
+      int64_t row = (int64_t)b * L + p;
+      if (k_new)
+        rc |= quantize_row(k_new + tok * IDX_DIM, IDX_DIM, k8 + row * IDX_DIM, k_scale + row);
+      if (kv_new) {
+        if (kv_fp8)
+          rc |= quantize_row(kv_new + tok * KV_DIM, KV_DIM, (uint8_t*)kv + row * KV_DIM,
+                             kv_scale + row);
+        else
+          memcpy((uint16_t*)kv + row * KV_DIM, kv_new + tok * KV_DIM, KV_DIM * sizeof(uint16_t));
+      }
+    }
+  }
+  free(seen);
+  return rc;
+}
+
 static int clamp_vis(int32_t v, int32_t L) {
   if (v < 0) return 0;
   if (v > L) return L;

@@ -43,6 +43,28 @@ double oracle_bf16(uint16_t bits);
 /* double -> bf16 bits, round to nearest even (finite inputs) */
 uint16_t oracle_round_bf16(double x);
 
+/* finite double -> E4M3 code: saturate to +-448, nearest code, ties to the
+ * even code, sign kept (so -0.0 and small negatives give 0x80) */
+uint8_t oracle_encode_e4m3(double v);
+
+/* Row quantisation. x [rows][D] bf16 -> codes [rows][D] E4M3, scales [rows]
+ * fp32: scale = fl32(max|x| / 448) (1 for an all-zero row), code =
+ * oracle_encode_e4m3(fl32(x / scale)). Rows with a non-finite value are
+ * rejected. */
+int oracle_quantize_e4m3(const uint16_t* x, int64_t rows, int32_t D, uint8_t* codes,
+                         float* scales);
+
+/* Cache append. k_new [B][T][128] bf16 (nullable), kv_new [B][T][576] bf16
+ * (nullable, not both NULL), pos [B][T]: token (b, t) goes to row pos[b,t] of
+ * sequence b; positions outside [0, L) are skipped, repeated positions within
+ * a sequence are rejected. Keys: k8 [B][L][128] codes + k_scale [B][L], by
+ * oracle_quantize_e4m3. Latents: kv [B][L][576] bf16 copied as is (kv_fp8 = 0)
+ * or quantised into codes + kv_scale [B][L] (kv_fp8 = 1). Rows not addressed
+ * are left untouched. */
+int oracle_cache_append(const uint16_t* k_new, const uint16_t* kv_new, int32_t kv_fp8,
+                        const int32_t* pos, int32_t B, int32_t T, int32_t L,
+                        uint8_t* k8, float* k_scale, void* kv, float* kv_scale);
+
 /* Indexer scores.
  * q8 [B][T][32][128] e4m3 codes, q_scale [B][T][32], w [B][T][32],
  * k8 [B][L][128] e4m3 codes, k_scale [B][L], vis_len [B][T] (clamped to

@@ -72,6 +72,139 @@ def test_round_bf16_against_torch_and_ties():
     assert oracle.round_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -30)) == 0xBF81  # just above a tie
 
 
+# ------------------------------------------------------------------ E4M3 encoding / quantisation
+def _finite_code_values():
+    return [(c, oracle.e4m3(c)) for c in range(256) if (c & 0x7F) != 0x7F]
+
+
+def test_encode_e4m3_round_trips_every_finite_code():
+    for c, v in _finite_code_values():
+        assert oracle.encode_e4m3(v) == c, (c, v)
+
+
+def test_encode_e4m3_matches_torch_float8_cast():
+    # torch's binary32 -> float8_e4m3fn cast rounds to nearest even; it does not
+    # saturate, so only |x| <= 448 is compared (saturation is pinned below)
+    x = (rng.standard_normal(6000) * 2.0 ** rng.integers(-12, 9, size=6000)).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    vals = sorted(v for c, v in _finite_code_values() if c < 0x80)
+    mids = np.array([(a + b) / 2 for a, b in zip(vals, vals[1:])], np.float32)  # exact ties
+    nxt = np.nextafter(mids, np.float32(np.inf))
+    prv = np.nextafter(mids, np.float32(0))
+    x = np.concatenate([x, mids, -mids, nxt, prv, -nxt])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.encode_e4m3(float(v)) for v in x], np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_encode_e4m3_ties_saturation_and_signed_zero():
+    vals = sorted(v for c, v in _finite_code_values() if c < 0x80)
+    for c in range(0x7E):  # every adjacent pair: the tie goes to the even code
+        m = (vals[c] + vals[c + 1]) / 2
+        assert oracle.encode_e4m3(m) == (c if c % 2 == 0 else c + 1), c
+        assert oracle.encode_e4m3(-m) == 0x80 | (c if c % 2 == 0 else c + 1), c
+    for v in (448.0, 460.0, 464.0, 1e4, 1e30):
+        assert oracle.encode_e4m3(v) == 0x7E and oracle.encode_e4m3(-v) == 0xFE
+    assert oracle.encode_e4m3(0.0) == 0x00 and oracle.encode_e4m3(-0.0) == 0x80
+    assert oracle.encode_e4m3(-2.0 ** -11) == 0x80  # rounds to zero, keeps the sign
+    assert oracle.encode_e4m3(2.0 ** -10 * 1.0000001) == 0x01  # just past the first tie
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("D", [128, 576])
+def test_quantize_recovers_codes_times_power_of_two_scale(D):
+    # x = dec(code) * 2^e with one entry at +-448 is exactly bf16, its amax is
+    # 448 * 2^e, so the scale is exactly 2^e and every code must come back
+    rs = np.random.default_rng(7 + D)
+    codes = _finite_codes(6 * D, rs).reshape(6, D)
+    exps = np.array([-20, -6, -1, 0, 3, 9])
+    for r in range(6):
+        codes[r, rs.integers(0, D)] = 0x7E if r % 2 == 0 else 0xFE
+    x = np.array([[oracle.e4m3(int(c)) * 2.0 ** int(e) for c in row] for row, e in zip(codes, exps)])
+    bits = _bf16_bits(x)
+    assert np.array_equal(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy(), x)
+    got_c, got_s = oracle.quantize_e4m3(bits)
+    assert np.array_equal(got_s, (2.0 ** exps).astype(np.float32))
+    # -0.0 codes decode to -0.0, which re-encodes as 0x80; 0x00 stays 0x00
+    assert np.array_equal(got_c, codes)
+
+
+def test_quantize_error_bound_and_zero_rows():
+    rs = np.random.default_rng(99)
+    x = (rs.standard_normal((40, 576)) * 10.0 ** rs.integers(-3, 3, size=(40, 1))).astype(np.float32)
+    x[3] = 0.0
+    x[4] = -0.0
+    x[5, :] = 0.0
+    x[5, 17] = -3.0  # one nonzero entry, negative
+    bits = _bf16_bits(x)
+    xb = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    codes, scales = oracle.quantize_e4m3(bits)
+    assert scales[3] == 1.0 and scales[4] == 1.0
+    assert np.all(codes[3] == 0x00) and np.all(codes[4] == 0x80)
+    assert scales[5] == np.float32(3.0 / 448.0) and codes[5, 17] == 0xFE
+    dec = np.vectorize(oracle.e4m3)(codes)
+    for r in range(40):
+        s = float(scales[r])
+        if r not in (3, 4):
+            assert s == np.float32(np.float32(np.abs(xb[r]).max()) / np.float32(448.0))
+        y = xb[r] / s
+        # nearest-code error: half a step, 2^-4 relative for normals, 2^-10 below 2^-6;
+        # slack for the binary32 quotient
+        bound = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) * (1 + 2.0 ** -20)
+        assert np.all(np.abs(dec[r] - y) <= bound), r
+        assert np.all(np.signbit(dec[r]) == np.signbit(xb[r]))
+        assert np.abs(dec[r]).max() == (448.0 if s != 1.0 or np.abs(xb[r]).max() else 0.0)
+
+
+def test_quantize_rejects_non_finite_rows():
+    bits = _bf16_bits(np.ones((2, 128), np.float32))
+    bits[1, 5] = 0x7F80  # +inf
+    with pytest.raises(ValueError):
+        oracle.quantize_e4m3(bits)
+
+
+def test_cache_append_writes_addressed_rows_only():
+    rs = np.random.default_rng(5)
+    B, T, L = 3, 4, 11
+    pos = np.array([[7, 8, 9, 10], [-1, 0, 11, 3], [2, 5, 40, -7]], np.int32)
+    k_codes = _finite_codes(B * T * 128, rs).reshape(B, T, 128)
+    k_codes[..., 0] = 0x7E
+    k_new = _bf16_bits(np.vectorize(oracle.e4m3)(k_codes) * 0.25)
+    kv_new = _bf16_bits(rs.standard_normal((B, T, 576)))
+    k8 = rs.integers(0, 256, size=(B, L, 128)).astype(np.uint8)
+    ks = rs.standard_normal((B, L)).astype(np.float32)
+    kvb = rs.integers(0, 1 << 16, size=(B, L, 576)).astype(np.uint16)
+    o_k8, o_ks, o_kv, _ = oracle.cache_append(k_new, kv_new, pos, k8, ks, kvb, None)
+    written = np.zeros((B, L), bool)
+    for b in range(B):
+        for t in range(T):
+            p = pos[b, t]
+            if 0 <= p < L:
+                written[b, p] = True
+                assert np.array_equal(o_k8[b, p], k_codes[b, t]) and o_ks[b, p] == 0.25
+                assert np.array_equal(o_kv[b, p], kv_new[b, t])
+    assert np.array_equal(o_k8[~written], k8[~written]) and np.array_equal(o_ks[~written], ks[~written])
+    assert np.array_equal(o_kv[~written], kvb[~written])
+    # FP8 latent cache: the rows are quantised like any other row
+    kv8 = rs.integers(0, 256, size=(B, L, 576)).astype(np.uint8)
+    kvs = np.zeros((B, L), np.float32)
+    _, _, o_kv8, o_kvs = oracle.cache_append(None, kv_new, pos, None, None, kv8, kvs)
+    c, s = oracle.quantize_e4m3(kv_new)
+    for b in range(B):
+        for t in range(T):
+            p = pos[b, t]
+            if 0 <= p < L:
+                assert np.array_equal(o_kv8[b, p], c[b, t]) and o_kvs[b, p] == s[b, t]
+    assert np.array_equal(o_kv8[~written], kv8[~written])
+    with pytest.raises(ValueError):  # two tokens of one sequence at one position
+        oracle.cache_append(None, kv_new, np.array([[1, 2, 1, 3]] * 3, np.int32), None, None,
+                            kvb, None)
+
+
 # ------------------------------------------------------------------ indexer
 def _idx_inputs(B, T, L, rs):
     q8 = _finite_codes(B * T * 32 * 128, rs).reshape(B, T, 32, 128)
