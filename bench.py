@@ -192,6 +192,53 @@ def kernel_breakdown(s, lcs, steps):
     return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
 
+def time_cache_append(w, lcs, steps):
+    """One cache append of a layer that keeps both caches: the B*T new tokens'
+    indexer keys (quantised) and latent rows (copied, or quantised for an FP8
+    cache) written at each sequence's next positions. Dedicated caches of
+    max(T, 4096) rows per sequence take the writes, so the step's inputs stay
+    as generated; the writes are the same scattered rows as in a full cache.
+    Returns (mean microseconds per launch, algorithmic bytes per launch)."""
+    import torch
+    dev = "cuda:0"
+    B, T = w.B, w.T
+    Lc = max(T, 4096)
+    g = torch.Generator(device=dev).manual_seed(7)
+    k_new = torch.randn((B, T, 128), generator=g, device=dev).to(torch.bfloat16)
+    kv_new = torch.randn((B, T, 576), generator=g, device=dev).to(torch.bfloat16)
+    pos = (torch.arange(T, dtype=torch.int32, device=dev) + (Lc - T)).repeat(B, 1).contiguous()
+    k8 = torch.zeros((B, Lc, 128), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((B, Lc), dtype=torch.float32, device=dev)
+    if w.kv_fp8:
+        kv = torch.zeros((B, Lc, 576), dtype=torch.uint8, device=dev)
+        kvs = torch.zeros((B, Lc), dtype=torch.float32, device=dev)
+    else:
+        kv = torch.zeros((B, Lc, 576), dtype=torch.bfloat16, device=dev)
+        kvs = None
+
+    def run(n):
+        for _ in range(n):
+            lcs.cache_append(pos, k_new=k_new, k8=k8, k_scale=ks, kv_new=kv_new, kv=kv,
+                             kv_scale=kvs)
+    # A launch this small takes less GPU time than one call through Python
+    # takes on the host, so the launches are captured once into a HIP graph
+    # (the kernel records no memset) and the graph is replayed: the time is
+    # then the GPU's own, as in a decode loop that replays its step.
+    run(3)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            run(steps)
+    torch.cuda.current_stream().wait_stream(cap)
+    us = timed(lambda n: [graph.replay() for _ in range(n)], 5, 2) * 1000.0 / steps
+    tok = B * T
+    nbytes = tok * (4 + 128 * 2 + 128 + 4 + 576 * 2 + (576 + 4 if w.kv_fp8 else 576 * 2))
+    return us, nbytes
+
+
 def step_bytes(w, off):
     """algorithmic HBM bytes of one step (keys+scales+queries, gathered rows and
     attention I/O); intermediates (scores, selections) are not counted"""
@@ -321,6 +368,11 @@ def main():
                                "avg_launch_us": round(idx_us, 2)}
         res["kernels_us"] = {k: round(v, 2) for k, v in ker.items()}
         res["launches_per_step"] = {k: v // max(args.steps // 2, 3) for k, v in counts.items()}
+        ap_us, ap_bytes = time_cache_append(w, lcs, 50)
+        res["cache_append"] = {"tokens": w.B * w.T, "us_per_launch": round(ap_us, 2),
+                               "bytes_per_launch": ap_bytes,
+                               "achieved_GBs": round(ap_bytes / (ap_us * 1e-6) / 1e9, 1),
+                               "note": "keys + latent rows of one layer; not part of the step"}
     if has_off:
         ms_off = timed(lambda n: run_composite(s, lcs, n, True), args.steps, args.warmup)
         res["indexshare"] = {"on_ms": round(ms, 4), "off_ms": round(ms_off, 4),

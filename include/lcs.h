@@ -169,6 +169,43 @@ lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers,
                                   void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
+/* Per-row FP8 quantisation. The pages keep the KV cache in FP8 (training
+ * section of "GLM-5.2 — 1M上下文开放权重的长程任务旗舰"; the `fp8_ds_mla` cache
+ * type of the vLLM launch in "IndexShare：省掉3/4的索引计算", Hygon DCU forum
+ * post) and name E4M3 as the release's FP8 format; the row scaling is a
+ * reading:
+ * x      [rows][D] bf16, finite values (other rows get unspecified bytes)
+ * codes  [rows][D] E4M3 output, scales [rows] fp32 output:
+ *   scale = fl32(max|x| / 448), or 1 for an all-zero row;
+ *   code  = E4M3(fl32(x / scale)), saturated at +-448, nearest, ties to the
+ *           even code, sign kept (so -0.0 gives 0x80).
+ * D is 128 (indexer keys; indexer queries, one row per (token, head)) or 576
+ * (latent KV rows). rows = 0 launches nothing. Decoding code * scale gives
+ * back x to within half an E4M3 step. */
+lcs_status lcs_quantize_e4m3(const uint16_t* x, int64_t rows, int32_t D, uint8_t* codes,
+                             float* scales, hipStream_t stream);
+
+/* Cache append: the T new tokens of each sequence enter the caches the
+ * indexer and attention read (same passages as lcs_quantize_e4m3).
+ * k_new  [B][T][128] bf16 indexer keys, or NULL for a layer that keeps no key
+ *        cache (an IndexShare layer that reuses another layer's selection);
+ *        k8 [B][L][128] and k_scale [B][L] receive the quantised rows (both
+ *        NULL when k_new is NULL)
+ * kv_new [B][T][576] bf16 latent rows, or NULL; kv [B][L][576] receives them
+ *        as bf16 (LCS_KV_BF16, kv_scale NULL) or as E4M3 codes with kv_scale
+ *        [B][L] (LCS_KV_FP8_E4M3), quantised as in lcs_quantize_e4m3
+ * pos    [B][T] int32 device array: token (b, t) goes to row pos[b,t] of
+ *        sequence b (a decode step at length n passes n; a prefill chunk or
+ *        an accepted draft run passes consecutive positions). Positions
+ *        outside [0, L) are skipped, so -1 marks a token not to store. Two
+ *        tokens of one sequence with the same position race (caller error,
+ *        not checked on the device).
+ * At least one of k_new and kv_new is given. Rows not addressed by pos are
+ * left as they are. */
+lcs_status lcs_cache_append(const uint16_t* k_new, const uint16_t* kv_new, lcs_kv_dtype kv_dtype,
+                            const int32_t* pos, int32_t B, int32_t T, int32_t L, uint8_t* k8,
+                            float* k_scale, void* kv, float* kv_scale, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* lcs_status_string(lcs_status s);
 /* Thread-local detail of this thread's last failed call ("" if none). */

@@ -16,7 +16,7 @@ __all__ = [
     "LcsError", "idx_score", "topk_workspace_bytes", "topk_select", "attn_workspace_bytes",
     "sparse_mla_attn", "count_full_layers", "indexshare_workspace_bytes", "indexshare_forward",
     "SCHED_GROUP4", "SCHED_GLM52", "SCHED_ALL_FULL", "SCHED_MASK", "KV_BF16", "KV_FP8_E4M3",
-    "LIB_PATH",
+    "LIB_PATH", "quantize_e4m3", "cache_append",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblcs.so")
@@ -57,6 +57,9 @@ _c_is_ws = _sig("lcs_indexshare_workspace_bytes", _sz, [_i32] * 4)
 _c_is = _sig("lcs_indexshare_forward", ctypes.c_int,
              [ctypes.POINTER(_Layer), _i32, ctypes.c_int, _p, _i32, ctypes.c_int, _p]
              + [_i32] * 4 + [_f32, _p, _p, _p, _sz, _p])
+_c_quant = _sig("lcs_quantize_e4m3", ctypes.c_int, [_p, ctypes.c_int64, _i32, _p, _p, _p])
+_c_append = _sig("lcs_cache_append", ctypes.c_int,
+                 [_p, _p, ctypes.c_int, _p] + [_i32] * 3 + [_p] * 5)
 _c_status = _sig("lcs_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_last = _sig("lcs_last_error", ctypes.c_char_p, [])
 
@@ -161,3 +164,23 @@ def indexshare_forward(layers, sched, vis_len, k, sm_scale, scores_scratch, idx_
                  _ptr(idx_out), _ptr(workspace),
                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
                  _stream(stream)))
+
+
+def quantize_e4m3(x, codes, scales, stream=None):
+    """codes[..., D] (uint8 E4M3) and scales[...] (fp32) from x[..., D] (bf16), D = 128 or
+    576: one scale per row, scale = max|x| / 448."""
+    D = x.shape[-1]
+    _check(_c_quant(_ptr(x), x.numel() // D if D else 0, D, _ptr(codes), _ptr(scales),
+                    _stream(stream)))
+
+
+def cache_append(pos, k_new=None, k8=None, k_scale=None, kv_new=None, kv=None, kv_scale=None,
+                 stream=None):
+    """Writes token (b, t) of k_new[B,T,128] / kv_new[B,T,576] (bf16) into row pos[b,t]
+    (int32) of k8[B,L,128] + k_scale[B,L] and of kv[B,L,576] (bf16, or uint8 E4M3 codes
+    with kv_scale[B,L]); positions outside [0, L) are skipped."""
+    B, T = pos.shape
+    L = (k8 if k8 is not None else kv).shape[1]
+    kd = _kv_dtype(kv) if kv is not None else KV_BF16
+    _check(_c_append(_ptr(k_new), _ptr(kv_new), kd, _ptr(pos), B, T, L, _ptr(k8), _ptr(k_scale),
+                     _ptr(kv), _ptr(kv_scale), _stream(stream)))

@@ -123,6 +123,36 @@ lcs_status validate_attn(const uint16_t* q, const void* kv, int kv_dtype, const 
   return LCS_OK;
 }
 
+lcs_status validate_append(const uint16_t* k_new, const uint16_t* kv_new, int kv_dtype,
+                           const int32_t* pos, int32_t B, int32_t T, int32_t L,
+                           const uint8_t* k8, const float* k_scale, const void* kv,
+                           const float* kv_scale) {
+  if (!k_new && !kv_new) return fail(LCS_ERR_NULL, "k_new and kv_new are both NULL");
+  REQUIRE(pos, "pos");
+  if (k_new) {
+    REQUIRE(k_new, "k_new");
+    REQUIRE(k8, "k8");
+    REQUIRE(k_scale, "k_scale");
+  } else if (k8 || k_scale) {
+    return fail(LCS_ERR_SHAPE, "k8 and k_scale must be NULL when k_new is NULL");
+  }
+  if (kv_dtype != LCS_KV_BF16 && kv_dtype != LCS_KV_FP8_E4M3)
+    return fail(LCS_ERR_UNSUPPORTED, "unknown kv_dtype %d", kv_dtype);
+  if (kv_new) {
+    REQUIRE(kv_new, "kv_new");
+    REQUIRE(kv, "kv");
+    if (kv_dtype == LCS_KV_FP8_E4M3) {
+      REQUIRE(kv_scale, "kv_scale");
+    } else if (kv_scale) {
+      return fail(LCS_ERR_SHAPE, "kv_scale must be NULL for bf16 kv");
+    }
+  } else if (kv || kv_scale) {
+    return fail(LCS_ERR_SHAPE, "kv and kv_scale must be NULL when kv_new is NULL");
+  }
+  TRY(check_dims(B, T, L));
+  return LCS_OK;
+}
+
 bool is_full_layer(lcs_sched sched, int32_t l, const uint8_t* mask) {
   switch (sched) {
     case LCS_SCHED_GROUP4:
@@ -195,6 +225,31 @@ lcs_status lcs_sparse_mla_attn(const uint16_t* q, const void* kv, lcs_kv_dtype k
   TRY(hip_status(lcs::launch_sparse_mla(q, kv, kv_dtype == LCS_KV_FP8_E4M3, kv_scale, idx, B, T,
                                         L, k, sm_scale, out, lse, workspace, stream),
                  "sparse_mla launch"));
+  return ok();
+}
+
+lcs_status lcs_quantize_e4m3(const uint16_t* x, int64_t rows, int32_t D, uint8_t* codes,
+                             float* scales, hipStream_t stream) {
+  if (D != LCS_IDX_DIM && D != LCS_KV_DIM)
+    return fail(LCS_ERR_UNSUPPORTED, "row width D = %d is not 128 or 576", D);
+  if (rows < 0 || rows > (1LL << 40) / D)
+    return fail(LCS_ERR_SHAPE, "rows = %lld outside [0, 2^40 / D]", (long long)rows);
+  if (rows == 0) return ok();
+  REQUIRE(x, "x");
+  REQUIRE(codes, "codes");
+  REQUIRE(scales, "scales");
+  TRY(hip_status(lcs::launch_quantize_e4m3(x, rows, D, codes, scales, stream),
+                 "quantize launch"));
+  return ok();
+}
+
+lcs_status lcs_cache_append(const uint16_t* k_new, const uint16_t* kv_new, lcs_kv_dtype kv_dtype,
+                            const int32_t* pos, int32_t B, int32_t T, int32_t L, uint8_t* k8,
+                            float* k_scale, void* kv, float* kv_scale, hipStream_t stream) {
+  TRY(validate_append(k_new, kv_new, (int)kv_dtype, pos, B, T, L, k8, k_scale, kv, kv_scale));
+  TRY(hip_status(lcs::launch_cache_append(k_new, kv_new, kv_dtype == LCS_KV_FP8_E4M3, pos, B, T,
+                                          L, k8, k_scale, kv, kv_scale, stream),
+                 "cache_append launch"));
   return ok();
 }
 

@@ -102,4 +102,11 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
                              int k, float sm_scale, uint16_t* out, float* lse,
                              void* workspace, hipStream_t stream);
 
+// D = 128 or 576
+hipError_t launch_quantize_e4m3(const uint16_t* x, int64_t rows, int D, uint8_t* codes,
+                                float* scales, hipStream_t stream);
+hipError_t launch_cache_append(const uint16_t* k_new, const uint16_t* kv_new, bool kv_fp8,
+                               const int32_t* pos, int B, int T, int L, uint8_t* k8,
+                               float* k_scale, void* kv, float* kv_scale, hipStream_t stream);
+
 }  // namespace lcs

@@ -21,12 +21,12 @@ _v, _i, _z, _f = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_floa
 
 def _declared():
     text = re.sub(r"/\*.*?\*/", "", open(HDR).read(), flags=re.S)
-    return sorted(set(re.findall(r"\b(lcs_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lcs_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_function():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -86,6 +86,33 @@ def test_attn_validation():
     assert call(k=4096) == UNSUP
     assert call(ws=None) == WS and call(wsb=need - 16) == WS
     assert call(lse=P + 8) == SHAPE
+
+
+def test_quantize_validation():
+    f = _fn("lcs_quantize_e4m3", [_v, ctypes.c_int64, _i, _v, _v, _v])
+    assert f(P, 10, 64, P, P, None) == UNSUP and b"128 or 576" in last()
+    assert f(P, -1, 128, P, P, None) == SHAPE
+    assert f(P, (1 << 40) // 128 + 1, 128, P, P, None) == SHAPE
+    assert f(None, 0, 128, None, None, None) == OK  # nothing to do, nothing launched
+    assert f(None, 4, 576, P, P, None) == NULL
+    assert f(P, 4, 576, P + 8, P, None) == SHAPE
+    assert f(P, 4, 128, P, None, None) == NULL
+
+
+def test_cache_append_validation():
+    f = _fn("lcs_cache_append", [_v, _v, ctypes.c_int, _v] + [_i] * 3 + [_v] * 5)
+    # (k_new, kv_new, dtype, pos, B, T, L, k8, k_scale, kv, kv_scale)
+    assert f(None, None, 0, P, 1, 1, 8, None, None, None, None, None) == NULL
+    assert b"both NULL" in last()
+    assert f(P, None, 0, None, 1, 1, 8, P, P, None, None, None) == NULL  # pos
+    assert f(P, None, 0, P, 1, 1, 8, P, None, None, None, None) == NULL  # k_scale
+    assert f(None, P, 0, P, 1, 1, 8, P, None, P, None, None) == SHAPE  # k8 without k_new
+    assert f(None, P, 0, P, 1, 1, 8, None, None, P, P, None) == SHAPE  # bf16 takes no scale
+    assert f(None, P, 1, P, 1, 1, 8, None, None, P, None, None) == NULL  # FP8 needs one
+    assert f(None, P, 5, P, 1, 1, 8, None, None, P, None, None) == UNSUP
+    assert f(P, None, 0, P, 1, 1, 8, P, P, P, None, None) == SHAPE  # kv without kv_new
+    assert f(P, P, 0, P, 1, 0, 8, P, P, P, None, None) == SHAPE
+    assert f(P, P, 0, P + 4, 1, 1, 8, P, P, P, None, None) == SHAPE
 
 
 def test_schedules_and_counts():
