@@ -18,7 +18,7 @@
 // The K order inside each P.V MFMA is a fixed permutation of the 32 rows,
 // chosen so that P^T comes straight out of the S^T accumulators.
 // With more than one split, normalised partial outputs (bf16: the final output
-// is bf16 too, and rounding the partials adds at most 2^-9 relative error) and
+// is bf16 too, and rounding the partials adds at most 2^-8 relative error) and
 // their log-sum-exp (fp32) are combined by a second kernel.
 #include "common.h"
 

@@ -195,3 +195,62 @@ def cache_append(k_new, kv_new, pos, k8, k_scale, kv, kv_scale):
     _check(_lib.oracle_cache_append(ptr(kn), ptr(vn), int(fp8), pos.ctypes.data, B, T, L,
                                     ptr(k8o), ptr(kso), ptr(kvo), ptr(kvso)), "cache_append")
     return k8o, kso, kvo, kvso
+
+
+_lib.oracle_topk_candidates.argtypes = [_p, _p] + [_i32] * 4 + [_p, _p]
+_lib.oracle_topk_merge.argtypes = [_p, _p] + [_i32] * 4 + [_p]
+_lib.oracle_idx_localize.argtypes = [_p] + [_i32] * 4 + [_p]
+_lib.oracle_lse_combine.argtypes = [_p, _p, _i32, _i32, _p, _p, _p]
+for _f in ("oracle_topk_candidates", "oracle_topk_merge", "oracle_idx_localize",
+           "oracle_lse_combine"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+def topk_candidates(scores, idx, pos_base):
+    """scores [..., L] f32, idx [..., k] i32 -> (cand_score [..., k], cand_idx [..., k])"""
+    s = _c(scores, np.float32)
+    ix = _c(idx, np.int32)
+    L, k = s.shape[-1], ix.shape[-1]
+    Q = ix.size // k
+    cs = np.empty(ix.shape, np.float32)
+    ci = np.empty(ix.shape, np.int32)
+    _check(_lib.oracle_topk_candidates(s.ctypes.data, ix.ctypes.data, Q, L, k, pos_base,
+                                       cs.ctypes.data, ci.ctypes.data), "topk_candidates")
+    return cs, ci
+
+
+def topk_merge(cand_score, cand_idx, k):
+    """cand_* [G, ..., k_in] -> idx [..., k]"""
+    cs = _c(cand_score, np.float32)
+    ci = _c(cand_idx, np.int32)
+    G, k_in = ci.shape[0], ci.shape[-1]
+    Q = ci.size // (G * k_in)
+    out = np.empty(ci.shape[1:-1] + (k,), np.int32)
+    _check(_lib.oracle_topk_merge(cs.ctypes.data, ci.ctypes.data, G, Q, k_in, k, out.ctypes.data),
+           "topk_merge")
+    return out
+
+
+def idx_localize(idx, lo, hi):
+    ix = _c(idx, np.int32)
+    k = ix.shape[-1]
+    out = np.empty_like(ix)
+    _check(_lib.oracle_idx_localize(ix.ctypes.data, ix.size // k, k, lo, hi, out.ctypes.data),
+           "idx_localize")
+    return out
+
+
+def lse_combine(part_out, part_lse, want64=False):
+    """part_out [G, ..., 64, 512] uint16 bf16 bits, part_lse [G, ..., 64] f32 ->
+    (out uint16 [..., 64, 512], lse f32 [..., 64][, out64])"""
+    po = _c(part_out, np.uint16)
+    pl = _c(part_lse, np.float32)
+    G = po.shape[0]
+    Q = po.size // (G * 64 * 512)
+    out = np.empty(po.shape[1:], np.uint16)
+    lse = np.empty(pl.shape[1:], np.float32)
+    o64 = np.empty(po.shape[1:], np.float64) if want64 else None
+    _check(_lib.oracle_lse_combine(po.ctypes.data, pl.ctypes.data, G, Q, out.ctypes.data,
+                                   lse.ctypes.data, o64.ctypes.data if want64 else None),
+           "lse_combine")
+    return (out, lse, o64) if want64 else (out, lse)

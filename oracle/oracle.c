@@ -261,6 +261,124 @@ int oracle_topk(const float* scores, const int32_t* vis_len, int32_t B,
   return 0;
 }
 
+/* ---- context-parallel halves of the selection and the attention ----
+ * Context parallelism splits the KV pool over devices (panel "CP · EP · P/D ·
+ * HiCache", ailearn special edition). Each shard holds the positions
+ * [lo, lo + L_shard) of every sequence and selects its own top-k; the
+ * definitions below turn those local selections into the selection over the
+ * whole sequence, and shard attention outputs into the whole attention. */
+
+/* A shard's selection as (score, global position) candidates: for each
+ * (query, slot) with idx >= 0, (scores[q][idx], idx + pos_base); empty slots
+ * give (-inf, -1). scores [Q][L], idx/cand_idx [Q][k], cand_score [Q][k]. */
+int oracle_topk_candidates(const float* scores, const int32_t* idx, int32_t Q, int32_t L,
+                           int32_t k, int32_t pos_base, float* cand_score, int32_t* cand_idx) {
+  if (!scores || !idx || !cand_score || !cand_idx || Q < 0 || L <= 0 || k <= 0) return 1;
+  for (int64_t q = 0; q < Q; ++q)
+    for (int32_t i = 0; i < k; ++i) {
+      int32_t p = idx[q * k + i];
+      if (p >= L) return 2;
+      cand_score[q * k + i] = p >= 0 ? scores[q * L + p] : -INFINITY;
+      cand_idx[q * k + i] = p >= 0 ? p + pos_base : -1;
+    }
+  return 0;
+}
+
+/* Selection from candidates: per query, the candidates with cand_idx >= 0
+ * ordered by (score descending, position ascending) -- the order of
+ * oracle_topk -- keep the first min(k, count), list them in ascending
+ * position order, pad with -1. cand_* [G][Q][k_in] (shard-major, as gathered
+ * from G shards); idx [Q][k]. Repeated positions or NaN scores: rejected. */
+int oracle_topk_merge(const float* cand_score, const int32_t* cand_idx, int32_t G, int32_t Q,
+                      int32_t k_in, int32_t k, int32_t* idx) {
+  if (!cand_score || !cand_idx || !idx || G <= 0 || Q < 0 || k_in <= 0 || k <= 0) return 1;
+  const size_t n = (size_t)G * k_in;
+  scored_pos* buf = (scored_pos*)malloc(sizeof(scored_pos) * n);
+  int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (n > (size_t)k ? n : (size_t)k));
+  if (!buf || !sel) { free(buf); free(sel); return 4; }
+  int rc = 0;
+  for (int64_t q = 0; q < Q && !rc; ++q) {
+    size_t m = 0;
+    for (int32_t g = 0; g < G; ++g)
+      for (int32_t i = 0; i < k_in; ++i) {
+        size_t at = ((size_t)g * Q + (size_t)q) * k_in + i;
+        if (cand_idx[at] < 0) continue;
+        if (isnan(cand_score[at])) rc = 3;
+        buf[m].score = cand_score[at];
+        buf[m].pos = cand_idx[at];
+        ++m;
+      }
+    for (size_t i = 0; i < m; ++i) sel[i] = buf[i].pos; /* repeated positions? */
+    qsort(sel, m, sizeof(int32_t), cmp_int);
+    for (size_t i = 1; i < m; ++i)
+      if (sel[i] == sel[i - 1]) rc = 5;
+    qsort(buf, m, sizeof(scored_pos), cmp_rank);
+    const size_t take = m < (size_t)k ? m : (size_t)k;
+    for (size_t i = 0; i < take; ++i) sel[i] = buf[i].pos;
+    qsort(sel, take, sizeof(int32_t), cmp_int);
+    for (int32_t i = 0; i < k; ++i) idx[q * k + i] = (size_t)i < take ? sel[i] : -1;
+  }
+  free(buf);
+  free(sel);
+  return rc;
+}
+
+/* A shard's share of an ascending selection: the entries in [lo, hi), in
+ * list order, minus lo, then -1. idx/local [Q][k]. */
+int oracle_idx_localize(const int32_t* idx, int32_t Q, int32_t k, int32_t lo, int32_t hi,
+                        int32_t* local) {
+  if (!idx || !local || Q < 0 || k <= 0 || lo < 0 || hi < lo) return 1;
+  for (int64_t q = 0; q < Q; ++q) {
+    int32_t m = 0;
+    for (int32_t i = 0; i < k; ++i) {
+      int32_t p = idx[q * k + i];
+      if (p >= lo && p < hi) local[q * k + m++] = p - lo;
+    }
+    for (; m < k; ++m) local[q * k + m] = -1;
+  }
+  return 0;
+}
+
+/* Attention from shard outputs. Shard g attended over the selected rows it
+ * holds, giving out_g (bf16) and lse_g = log sum_{i in g} exp(z_i). Over all
+ * rows, sum_i e^{z_i} v_i / sum_i e^{z_i} = sum_g e^{lse_g} out_g / sum_g
+ * e^{lse_g}: with M = max_g lse_g and w_g = exp(lse_g - M),
+ * out = sum_g w_g out_g / sum_g w_g and lse = M + log sum_g w_g, in double;
+ * shards with lse = -inf weigh nothing; all -inf gives out = 0, lse = -inf.
+ * part_out [G][Q][64][512] bf16, part_lse [G][Q][64] -> out [Q][64][512]
+ * bf16 (RNE), lse [Q][64] fp32; out64 (nullable) gets the unrounded out. */
+int oracle_lse_combine(const uint16_t* part_out, const float* part_lse, int32_t G, int32_t Q,
+                       uint16_t* out, float* lse, double* out64) {
+  if (!part_out || !part_lse || !out || G <= 0 || Q < 0) return 1;
+  const size_t per = (size_t)ATT_HEADS * KV_LATENT;
+  for (size_t q = 0; q < (size_t)Q; ++q)
+    for (int h = 0; h < ATT_HEADS; ++h) {
+      double M = -INFINITY;
+      for (int32_t g = 0; g < G; ++g) {
+        double l = part_lse[((size_t)g * Q + q) * ATT_HEADS + h];
+        if (isnan(l) || l == INFINITY) return 3;
+        if (l > M) M = l;
+      }
+      double wsum = 0.0;
+      for (int v = 0; v < KV_LATENT; ++v) {
+        double acc = 0.0;
+        wsum = 0.0;
+        for (int32_t g = 0; g < G; ++g) {
+          double l = part_lse[((size_t)g * Q + q) * ATT_HEADS + h];
+          if (l == -INFINITY) continue;
+          double w = exp(l - M);
+          wsum += w;
+          acc += w * oracle_bf16(part_out[((size_t)g * Q + q) * per + (size_t)h * KV_LATENT + v]);
+        }
+        double o = wsum > 0.0 ? acc / wsum : 0.0;
+        out[q * per + (size_t)h * KV_LATENT + v] = oracle_round_bf16(o);
+        if (out64) out64[q * per + (size_t)h * KV_LATENT + v] = o;
+      }
+      if (lse) lse[q * ATT_HEADS + h] = M == -INFINITY ? -INFINITY : (float)(M + log(wsum));
+    }
+  return 0;
+}
+
 int oracle_sparse_mla(const uint16_t* q, const void* kv, int32_t kv_fp8,
                       const float* kv_scale, const int32_t* idx, int32_t B,
                       int32_t T, int32_t L, int32_t k, double sm_scale,

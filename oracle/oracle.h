@@ -97,6 +97,25 @@ int oracle_sparse_mla(const uint16_t* q, const void* kv, int32_t kv_fp8,
                       int32_t T, int32_t L, int32_t k, double sm_scale,
                       uint16_t* out, float* lse, double* out64);
 
+/* Context-parallel halves (a shard holds positions [lo, lo + L_shard)):
+ * candidates of a shard's selection: (scores[q][idx], idx + pos_base), or
+ * (-inf, -1) for an empty slot. scores [Q][L], idx [Q][k]. */
+int oracle_topk_candidates(const float* scores, const int32_t* idx, int32_t Q, int32_t L,
+                           int32_t k, int32_t pos_base, float* cand_score, int32_t* cand_idx);
+/* selection from G shards' candidates cand_* [G][Q][k_in] (cand_idx < 0 =
+ * none): order by (score desc, position asc), keep min(k, count), ascending,
+ * -1 padded, idx [Q][k]. Repeated positions and NaN scores are rejected. */
+int oracle_topk_merge(const float* cand_score, const int32_t* cand_idx, int32_t G, int32_t Q,
+                      int32_t k_in, int32_t k, int32_t* idx);
+/* entries of each ascending list idx [Q][k] in [lo, hi), minus lo, then -1 */
+int oracle_idx_localize(const int32_t* idx, int32_t Q, int32_t k, int32_t lo, int32_t hi,
+                        int32_t* local);
+/* out = sum_g w_g out_g / sum_g w_g, w_g = exp(lse_g - max lse), lse = max +
+ * log sum w, in double. part_out [G][Q][64][512] bf16, part_lse [G][Q][64];
+ * out [Q][64][512] bf16, lse [Q][64] (nullable), out64 (nullable). */
+int oracle_lse_combine(const uint16_t* part_out, const float* part_lse, int32_t G, int32_t Q,
+                       uint16_t* out, float* lse, double* out64);
+
 /* IndexShare layer schedules */
 enum { ORACLE_SCHED_GROUP4 = 0, ORACLE_SCHED_GLM52 = 1, ORACLE_SCHED_ALL_FULL = 2,
        ORACLE_SCHED_MASK = 3 };

@@ -110,11 +110,6 @@ def test_encode_e4m3_ties_saturation_and_signed_zero():
     assert oracle.encode_e4m3(2.0 ** -10 * 1.0000001) == 0x01  # just past the first tie
 
 
-def _bf16_bits(x):
-    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16) \
-        .numpy().view(np.uint16)
-
-
 @pytest.mark.parametrize("D", [128, 576])
 def test_quantize_recovers_codes_times_power_of_two_scale(D):
     # x = dec(code) * 2^e with one entry at +-448 is exactly bf16, its amax is
@@ -523,3 +518,115 @@ def test_mtp_steps_reuse_step0_selection_and_kv():
         layers[s]["q"] = layers[0]["q"]
     outs, _, _ = oracle.indexshare(layers, 0, vis, k, 1 / 24, kv_fp8=True, mtp_steps=7)
     assert all(np.array_equal(outs[0], outs[s]) for s in range(7))
+
+
+# ------------------------------------------------------------------ context-parallel halves
+def _shard_bounds(L, G, rs):
+    cuts = np.sort(rs.choice(np.arange(1, L), size=G - 1, replace=False)) if G > 1 else []
+    b = [0] + list(cuts) + [L]
+    return list(zip(b[:-1], b[1:]))
+
+
+@pytest.mark.parametrize("G", [1, 3, 8])
+def test_topk_merge_of_shard_selections_equals_whole_row_selection(G):
+    # the whole row's top-k lies inside the union of the shards' top-k's, and the
+    # merge orders candidates as the whole-row selection does, so merging the
+    # shards' selections must give oracle_topk of the whole row exactly; heavy
+    # ties (scores from 7 values) make the position tie-break decide most slots
+    rs = np.random.default_rng(300 + G)
+    Q, L, k = 9, 700, 64
+    scores = rs.choice(np.array([-2.5, -1.0, 0.0, 0.5, 1.0, 3.0, 7.25], np.float32), size=(Q, L))
+    scores[0] = 1.0  # all equal
+    vis = np.array([L, L, 5, 0, 64, 65, 300, 699, 1], np.int32)
+    whole = oracle.topk(scores[:, None, :], vis[:, None], k)[:, 0]
+    bounds = _shard_bounds(L, G, rs)
+    cs, ci = [], []
+    for lo, hi in bounds:
+        lvis = np.clip(vis - lo, 0, hi - lo).astype(np.int32)
+        local = oracle.topk(np.ascontiguousarray(scores[:, None, lo:hi]), lvis[:, None], k)[:, 0]
+        c = oracle.topk_candidates(np.ascontiguousarray(scores[:, lo:hi]), local, lo)
+        assert np.all((c[1] == -1) == (local == -1))
+        cs.append(c[0])
+        ci.append(c[1])
+    merged = oracle.topk_merge(np.stack(cs), np.stack(ci), k)
+    assert np.array_equal(merged, whole)
+    # each shard's share of the whole selection, shifted back, is that selection
+    back = []
+    for lo, hi in bounds:
+        loc = oracle.idx_localize(whole, lo, hi)
+        for q in range(Q):
+            row = loc[q]
+            n = int((row >= 0).sum())
+            assert np.all(row[n:] == -1) and np.all(np.diff(row[:n]) > 0)
+            assert np.all(row[:n] < hi - lo)
+        back.append(np.where(loc >= 0, loc + lo, -1))
+    for q in range(Q):
+        got = np.sort(np.concatenate([b[q][b[q] >= 0] for b in back]))
+        assert np.array_equal(got, whole[q][whole[q] >= 0])
+
+
+def test_topk_merge_edge_cases():
+    cs = np.array([[[5.0, 1.0, -np.inf]], [[5.0, 9.0, 2.0]]], np.float32)  # [G=2][Q=1][3]
+    ci = np.array([[[30, 2, -1]], [[7, 40, -1]]], np.int32)
+    assert oracle.topk_merge(cs, ci, 2).tolist() == [[7, 40]]  # 9, then 5 at the lower position
+    assert oracle.topk_merge(cs, ci, 3).tolist() == [[7, 30, 40]]
+    assert oracle.topk_merge(cs, ci, 6).tolist() == [[2, 7, 30, 40, -1, -1]]  # empty slots never
+    with pytest.raises(ValueError):  # one position offered twice
+        oracle.topk_merge(cs, np.array([[[30, 2, -1]], [[30, 40, -1]]], np.int32), 2)
+    with pytest.raises(ValueError):
+        oracle.topk_merge(np.where(cs == 1.0, np.nan, cs).astype(np.float32), ci, 2)
+    none = np.full((1, 1, 3), -1, np.int32)
+    assert oracle.topk_merge(cs[:1], none, 2).tolist() == [[-1, -1]]
+
+
+def _shard_attention(q, kv, idx, bounds, sm):
+    po, pl = [], []
+    for lo, hi in bounds:
+        loc = oracle.idx_localize(idx, lo, hi)
+        o, l = oracle.sparse_mla(q, np.ascontiguousarray(kv[:, lo:hi]), None, loc, sm)
+        po.append(o)
+        pl.append(l)
+    return np.stack(po), np.stack(pl)
+
+
+@pytest.mark.parametrize("G", [2, 5])
+def test_lse_combine_of_shard_attention_equals_whole_attention(G):
+    rs = np.random.default_rng(400 + G)
+    B, T, L, k, sm = 2, 1, 96, 40, 1 / 24
+    q = _bf16_bits(rs.standard_normal((B, T, 64, 576)) * 2)
+    kv = _bf16_bits(rs.standard_normal((B, L, 576)))
+    idx = np.stack([np.sort(rs.choice(L, size=k, replace=False)) for _ in range(B * T)]).reshape(
+        B, T, k).astype(np.int32)
+    idx[1, 0, -7:] = -1
+    ref_o, ref_l, ref64 = oracle.sparse_mla(q, kv, None, idx, sm, want64=True)
+    bounds = _shard_bounds(L, G, rs)
+    po, pl = _shard_attention(q, kv, idx, bounds, sm)
+    out, lse, out64 = oracle.lse_combine(po, pl, want64=True)
+    # each shard output carries at most half a bf16 step (8 significant bits:
+    # 2^-8 relative), so the weighted mean is within 2^-8 of the largest shard
+    # value per element
+    bound = 2.0 ** -8 * np.abs(_bits_to_f64(po)).max(axis=0) + 1e-12
+    assert np.all(np.abs(out64 - ref64) <= bound)
+    assert np.allclose(lse, ref_l, rtol=1e-6, atol=1e-6)
+    assert np.array_equal(out, np.vectorize(oracle.round_bf16, otypes=[np.uint16])(out64))
+
+
+def test_lse_combine_special_cases():
+    rs = np.random.default_rng(7)
+    po = _bf16_bits(rs.standard_normal((3, 2, 64, 512)))
+    pl = rs.standard_normal((3, 2, 64)).astype(np.float32) * 4
+    o1, l1 = oracle.lse_combine(po[:1], pl[:1])
+    assert np.array_equal(o1, po[0]) and np.array_equal(l1, pl[0])  # one shard: identity
+    pe = pl.copy()
+    pe[1:] = -np.inf  # shards with no selected row weigh nothing
+    o2, l2 = oracle.lse_combine(po, pe)
+    assert np.array_equal(o2, po[0]) and np.array_equal(l2, pl[0])
+    o3, l3 = oracle.lse_combine(po, np.full_like(pl, -np.inf))
+    assert np.all(o3 == 0) and np.all(l3 == -np.inf)
+    o4, l4 = oracle.lse_combine(np.stack([po[0], po[0]]), np.stack([pl[0], pl[0]]))
+    assert np.array_equal(o4, po[0])  # two equal shards: the same mean, twice the mass
+    assert np.allclose(l4, pl[0].astype(np.float64) + np.log(2.0), rtol=0, atol=1e-6)
+    hi = pl.copy()
+    hi[0] += 60.0  # one shard dominates: the others' weights fall below 2^-80
+    o5, _ = oracle.lse_combine(po, hi)
+    assert np.array_equal(o5, po[0])
