@@ -224,19 +224,62 @@ def time_cache_append(w, lcs, steps):
     # takes on the host, so the launches are captured once into a HIP graph
     # (the kernel records no memset) and the graph is replayed: the time is
     # then the GPU's own, as in a decode loop that replays its step.
+    us = _graph_us(run, steps)
+    tok = B * T
+    nbytes = tok * (4 + 128 * 2 + 128 + 4 + 576 * 2 + (576 + 4 if w.kv_fp8 else 576 * 2))
+    return us, nbytes
+
+
+def _graph_us(run, n):
+    """mean microseconds per launch of n launches captured into one HIP graph
+    and replayed (launches too short for Python to keep the GPU busy)"""
+    import torch
     run(3)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            run(steps)
+    with torch.cuda.graph(graph, stream=cap):
+        run(n)
     torch.cuda.current_stream().wait_stream(cap)
-    us = timed(lambda n: [graph.replay() for _ in range(n)], 5, 2) * 1000.0 / steps
-    tok = B * T
-    nbytes = tok * (4 + 128 * 2 + 128 + 4 + 576 * 2 + (576 + 4 if w.kv_fp8 else 576 * 2))
-    return us, nbytes
+    return timed(lambda m: [graph.replay() for _ in range(m)], 5, 2) * 1000.0 / n
+
+
+def time_context_parallel(w, lcs, G=8, n=50):
+    """The single-device halves of G-way context parallelism for one full layer
+    of the workload's queries: one shard's candidate gather, the merge of G x k
+    candidates, one shard's localisation and the LSE combine of G shard
+    outputs. Inputs are random tensors of the real shapes (scores N(0,1),
+    distinct positions), resident in HBM. Returns {kernel: (us, bytes)}."""
+    import torch
+    dev = "cuda:0"
+    Q, k = w.B * w.T, w.k
+    Ls = w.L // G
+    g = torch.Generator(device=dev).manual_seed(11)
+    scores = torch.randn((Q, 1, Ls), generator=g, device=dev)
+    idx = torch.stack([torch.sort(torch.randperm(Ls, generator=g, device=dev)[:k])[0]
+                       for _ in range(Q)]).to(torch.int32).view(Q, 1, k)
+    cs = torch.empty((G, Q, 1, k), dtype=torch.float32, device=dev)
+    ci = torch.empty((G, Q, 1, k), dtype=torch.int32, device=dev)
+    for sh in range(G):
+        lcs.topk_candidates(scores, idx, sh * Ls, cs[sh], ci[sh])
+    merged = torch.empty((Q, 1, k), dtype=torch.int32, device=dev)
+    local = torch.empty_like(merged)
+    po = torch.randn((G, Q, 1, 64, 512), generator=g, device=dev).to(torch.bfloat16)
+    pl = torch.randn((G, Q, 1, 64), generator=g, device=dev)
+    out = torch.empty((Q, 1, 64, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Q, 1, 64), dtype=torch.float32, device=dev)
+    res = {}
+    res["topk_candidates"] = (_graph_us(lambda m: [lcs.topk_candidates(
+        scores, idx, Ls, cs[1], ci[1]) for _ in range(m)], n), Q * k * (4 + 4 + 4 + 4))
+    res["topk_merge"] = (_graph_us(lambda m: [lcs.topk_merge(cs, ci, k, merged)
+                                              for _ in range(m)], n), Q * (G * k * 8 + k * 4))
+    res["idx_localize"] = (_graph_us(lambda m: [lcs.idx_localize(merged, Ls, 2 * Ls, local)
+                                                for _ in range(m)], n), Q * k * 8)
+    res["lse_combine"] = (_graph_us(lambda m: [lcs.lse_combine(po, pl, out, lse)
+                                               for _ in range(m)], n),
+                          Q * ((G + 1) * (64 * 512 * 2 + 64 * 4)))
+    return res
 
 
 def step_bytes(w, off):
@@ -373,6 +416,13 @@ def main():
                                "bytes_per_launch": ap_bytes,
                                "achieved_GBs": round(ap_bytes / (ap_us * 1e-6) / 1e9, 1),
                                "note": "keys + latent rows of one layer; not part of the step"}
+        if w.T < IDX_PREFILL_MIN_T:
+            cp = time_context_parallel(w, lcs)
+            res["context_parallel"] = {
+                "shards": 8, "note": "single-device halves of 8-way context parallelism for one "
+                "full layer; not part of the step",
+                "us_per_launch": {kk: round(v[0], 2) for kk, v in cp.items()},
+                "bytes_per_launch": {kk: v[1] for kk, v in cp.items()}}
     if has_off:
         ms_off = timed(lambda n: run_composite(s, lcs, n, True), args.steps, args.warmup)
         res["indexshare"] = {"on_ms": round(ms, 4), "off_ms": round(ms_off, 4),

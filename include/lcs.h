@@ -64,6 +64,8 @@ typedef enum { LCS_KV_BF16 = 0, LCS_KV_FP8_E4M3 = 1 } lcs_kv_dtype;
 #define LCS_KV_ROPE 64
 #define LCS_KV_DIM 576
 #define LCS_MAX_TOPK 2048
+#define LCS_MAX_MERGE_CANDIDATES 32768 /* G * k_in of lcs_topk_merge */
+#define LCS_MAX_SHARDS 1024            /* G of lcs_lse_combine */
 
 /* Indexer scores ("Indexer 先扫历史": every cached position is scored).
  * q8      [B][T][32][128] E4M3 query codes
@@ -205,6 +207,62 @@ lcs_status lcs_quantize_e4m3(const uint16_t* x, int64_t rows, int32_t D, uint8_t
 lcs_status lcs_cache_append(const uint16_t* k_new, const uint16_t* kv_new, lcs_kv_dtype kv_dtype,
                             const int32_t* pos, int32_t B, int32_t T, int32_t L, uint8_t* k8,
                             float* k_scale, void* kv, float* kv_scale, hipStream_t stream);
+
+/* Context parallelism: the single-device halves. Context parallelism splits
+ * the KV pool over devices (panel "CP · EP · P/D · HiCache", ailearn GLM-5.2
+ * special edition); the pages do not say how the selection and the attention
+ * are put back together. A shard holds positions [lo, lo + L_shard) of every
+ * sequence (its own k8/kv of L = L_shard rows, vis_len clamped to the shard)
+ * and runs lcs_idx_score + lcs_topk_select on them. The whole sequence's
+ * top-k lies inside the union of the shards' top-k's, so:
+ *   1. lcs_topk_candidates turns each shard's selection into (score, global
+ *      position) pairs;
+ *   2. the pairs of all G shards are gathered (on one device: written side by
+ *      side; across devices: an all-gather) as cand_* [G][B][T][k_in];
+ *   3. lcs_topk_merge selects from them exactly what lcs_topk_select would
+ *      have selected over the whole sequence;
+ *   4. lcs_idx_localize gives each shard its share of the merged list;
+ *      each shard runs lcs_sparse_mla_attn with it over its own rows;
+ *   5. lcs_lse_combine merges the G shard outputs [G][B][T][...] (gathered
+ *      likewise) into the attention over all selected rows. */
+
+/* Candidates of one shard's selection.
+ * scores [B][T][L] fp32 (the shard's lcs_idx_score output), idx [B][T][k]
+ * (its lcs_topk_select output) -> cand_score [B][T][k] fp32 and cand_idx
+ * [B][T][k] int32: (scores[b,t,idx], idx + pos_base) per slot; an empty slot
+ * (idx outside [0, L)) gives (-inf, -1). pos_base = the shard's first
+ * position, with pos_base + L <= 2^31 - 1. */
+lcs_status lcs_topk_candidates(const float* scores, const int32_t* idx, int32_t B, int32_t T,
+                               int32_t L, int32_t k, int32_t pos_base, float* cand_score,
+                               int32_t* cand_idx, hipStream_t stream);
+
+/* Selection from the candidates of G shards.
+ * cand_score/cand_idx [G][B][T][k_in] (cand_idx < 0 = no candidate) ->
+ * idx [B][T][k]: the min(k, count) candidates with the largest scores, equal
+ * scores broken by the lower position and -0.0 equal to +0.0 (the order of
+ * lcs_topk_select), listed in ascending position order and padded with -1.
+ * Exact. G * k_in <= LCS_MAX_MERGE_CANDIDATES, k in [1, 2048]. A position
+ * offered twice for one query is a caller error (the output stays within
+ * idx, its content is then unspecified); scores must not be NaN. */
+lcs_status lcs_topk_merge(const float* cand_score, const int32_t* cand_idx, int32_t G, int32_t B,
+                          int32_t T, int32_t k_in, int32_t k, int32_t* idx, hipStream_t stream);
+
+/* A shard's share of a selection: local [B][T][k] = the entries of idx
+ * [B][T][k] in [lo, hi), in list order, minus lo, then -1 (so an ascending
+ * list gives an ascending local list, ready for lcs_sparse_mla_attn over the
+ * shard's rows). idx and local must not alias. */
+lcs_status lcs_idx_localize(const int32_t* idx, int32_t B, int32_t T, int32_t k, int32_t lo,
+                            int32_t hi, int32_t* local, hipStream_t stream);
+
+/* Attention from shard outputs.
+ * part_out [G][B][T][64][512] bf16 and part_lse [G][B][T][64] fp32 (natural
+ * log; -inf for a shard with no selected row), as lcs_sparse_mla_attn writes
+ * them per shard -> out [B][T][64][512] bf16 and lse [B][T][64] (nullable):
+ *   out = sum_g e^(lse_g - M) out_g / sum_g e^(lse_g - M), M = max_g lse_g,
+ *   lse = M + log sum_g e^(lse_g - M);
+ * all shards empty: out = 0, lse = -inf. G in [1, LCS_MAX_SHARDS]. */
+lcs_status lcs_lse_combine(const uint16_t* part_out, const float* part_lse, int32_t G, int32_t B,
+                           int32_t T, uint16_t* out, float* lse, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* lcs_status_string(lcs_status s);

@@ -16,7 +16,8 @@ __all__ = [
     "LcsError", "idx_score", "topk_workspace_bytes", "topk_select", "attn_workspace_bytes",
     "sparse_mla_attn", "count_full_layers", "indexshare_workspace_bytes", "indexshare_forward",
     "SCHED_GROUP4", "SCHED_GLM52", "SCHED_ALL_FULL", "SCHED_MASK", "KV_BF16", "KV_FP8_E4M3",
-    "LIB_PATH", "quantize_e4m3", "cache_append",
+    "LIB_PATH", "quantize_e4m3", "cache_append", "topk_candidates", "topk_merge", "idx_localize",
+    "lse_combine",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblcs.so")
@@ -60,6 +61,10 @@ _c_is = _sig("lcs_indexshare_forward", ctypes.c_int,
 _c_quant = _sig("lcs_quantize_e4m3", ctypes.c_int, [_p, ctypes.c_int64, _i32, _p, _p, _p])
 _c_append = _sig("lcs_cache_append", ctypes.c_int,
                  [_p, _p, ctypes.c_int, _p] + [_i32] * 3 + [_p] * 5)
+_c_cand = _sig("lcs_topk_candidates", ctypes.c_int, [_p, _p] + [_i32] * 5 + [_p, _p, _p])
+_c_merge = _sig("lcs_topk_merge", ctypes.c_int, [_p, _p] + [_i32] * 5 + [_p, _p])
+_c_local = _sig("lcs_idx_localize", ctypes.c_int, [_p] + [_i32] * 5 + [_p, _p])
+_c_comb = _sig("lcs_lse_combine", ctypes.c_int, [_p, _p] + [_i32] * 3 + [_p, _p, _p])
 _c_status = _sig("lcs_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_last = _sig("lcs_last_error", ctypes.c_char_p, [])
 
@@ -184,3 +189,33 @@ def cache_append(pos, k_new=None, k8=None, k_scale=None, kv_new=None, kv=None, k
     kd = _kv_dtype(kv) if kv is not None else KV_BF16
     _check(_c_append(_ptr(k_new), _ptr(kv_new), kd, _ptr(pos), B, T, L, _ptr(k8), _ptr(k_scale),
                      _ptr(kv), _ptr(kv_scale), _stream(stream)))
+
+
+def topk_candidates(scores, idx, pos_base, cand_score, cand_idx, stream=None):
+    """cand_score/cand_idx[B,T,k] = (scores[b,t,idx], idx + pos_base) of one shard's
+    selection idx[B,T,k] over its scores[B,T,L]; (-inf, -1) for empty slots."""
+    B, T, L = scores.shape
+    k = idx.shape[-1]
+    _check(_c_cand(_ptr(scores), _ptr(idx), B, T, L, k, int(pos_base), _ptr(cand_score),
+                   _ptr(cand_idx), _stream(stream)))
+
+
+def topk_merge(cand_score, cand_idx, k, idx, stream=None):
+    """idx[B,T,k] from the candidates cand_*[G,B,T,k_in] of G shards."""
+    G, B, T, k_in = cand_idx.shape
+    _check(_c_merge(_ptr(cand_score), _ptr(cand_idx), G, B, T, k_in, k, _ptr(idx),
+                    _stream(stream)))
+
+
+def idx_localize(idx, lo, hi, local, stream=None):
+    """local[B,T,k] = entries of idx[B,T,k] in [lo, hi), minus lo, then -1."""
+    B, T, k = idx.shape
+    _check(_c_local(_ptr(idx), B, T, k, int(lo), int(hi), _ptr(local), _stream(stream)))
+
+
+def lse_combine(part_out, part_lse, out, lse=None, stream=None):
+    """out[B,T,64,512] (and lse[B,T,64]) from G shard outputs part_out[G,B,T,64,512] (bf16)
+    and part_lse[G,B,T,64] (fp32, natural log)."""
+    G, B, T = part_out.shape[:3]
+    _check(_c_comb(_ptr(part_out), _ptr(part_lse), G, B, T, _ptr(out), _ptr(lse),
+                   _stream(stream)))

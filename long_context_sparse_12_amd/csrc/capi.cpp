@@ -253,6 +253,68 @@ lcs_status lcs_cache_append(const uint16_t* k_new, const uint16_t* kv_new, lcs_k
   return ok();
 }
 
+lcs_status lcs_topk_candidates(const float* scores, const int32_t* idx, int32_t B, int32_t T,
+                               int32_t L, int32_t k, int32_t pos_base, float* cand_score,
+                               int32_t* cand_idx, hipStream_t stream) {
+  REQUIRE(scores, "scores");
+  REQUIRE(idx, "idx");
+  REQUIRE(cand_score, "cand_score");
+  REQUIRE(cand_idx, "cand_idx");
+  TRY(check_dims(B, T, L));
+  TRY(check_k(k));
+  if (pos_base < 0 || (int64_t)pos_base + L > 0x7FFFFFFF)
+    return fail(LCS_ERR_SHAPE, "pos_base = %d: positions pos_base + [0, L) must fit in int32",
+                pos_base);
+  TRY(hip_status(lcs::launch_topk_candidates(scores, idx, (int64_t)B * T, L, k, pos_base,
+                                             cand_score, cand_idx, stream),
+                 "topk_candidates launch"));
+  return ok();
+}
+
+lcs_status lcs_topk_merge(const float* cand_score, const int32_t* cand_idx, int32_t G, int32_t B,
+                          int32_t T, int32_t k_in, int32_t k, int32_t* idx, hipStream_t stream) {
+  REQUIRE(cand_score, "cand_score");
+  REQUIRE(cand_idx, "cand_idx");
+  REQUIRE(idx, "idx");
+  if (G <= 0 || k_in <= 0) return fail(LCS_ERR_SHAPE, "G and k_in must be positive");
+  if ((int64_t)G * k_in > LCS_MAX_MERGE_CANDIDATES)
+    return fail(LCS_ERR_UNSUPPORTED, "G * k_in = %lld exceeds %d candidates per query",
+                (long long)G * k_in, LCS_MAX_MERGE_CANDIDATES);
+  TRY(check_dims(B, T, 1));
+  TRY(check_k(k));
+  TRY(hip_status(lcs::launch_topk_merge(cand_score, cand_idx, G, (int64_t)B * T, k_in, k, idx,
+                                        stream),
+                 "topk_merge launch"));
+  return ok();
+}
+
+lcs_status lcs_idx_localize(const int32_t* idx, int32_t B, int32_t T, int32_t k, int32_t lo,
+                            int32_t hi, int32_t* local, hipStream_t stream) {
+  REQUIRE(idx, "idx");
+  REQUIRE(local, "local");
+  if (idx == local) return fail(LCS_ERR_SHAPE, "idx and local must not alias");
+  TRY(check_dims(B, T, 1));
+  TRY(check_k(k));
+  if (lo < 0 || hi < lo) return fail(LCS_ERR_SHAPE, "need 0 <= lo <= hi (got %d, %d)", lo, hi);
+  TRY(hip_status(lcs::launch_idx_localize(idx, (int64_t)B * T, k, lo, hi, local, stream),
+                 "idx_localize launch"));
+  return ok();
+}
+
+lcs_status lcs_lse_combine(const uint16_t* part_out, const float* part_lse, int32_t G, int32_t B,
+                           int32_t T, uint16_t* out, float* lse, hipStream_t stream) {
+  REQUIRE(part_out, "part_out");
+  REQUIRE(part_lse, "part_lse");
+  REQUIRE(out, "out");
+  if (lse && !aligned16(lse)) return fail(LCS_ERR_SHAPE, "lse is not 16-byte aligned");
+  if (G <= 0 || G > LCS_MAX_SHARDS)
+    return fail(LCS_ERR_SHAPE, "G = %d outside [1, %d]", G, LCS_MAX_SHARDS);
+  TRY(check_dims(B, T, 1));
+  TRY(hip_status(lcs::launch_lse_combine(part_out, part_lse, G, (int64_t)B * T, out, lse, stream),
+                 "lse_combine launch"));
+  return ok();
+}
+
 int32_t lcs_count_full_layers(lcs_sched sched, int32_t n_layers, const uint8_t* full_mask,
                               int32_t mtp_steps) {
   if (n_layers <= 0 || mtp_steps < 0) return -1;

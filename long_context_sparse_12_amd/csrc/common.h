@@ -109,4 +109,15 @@ hipError_t launch_cache_append(const uint16_t* k_new, const uint16_t* kv_new, bo
                                const int32_t* pos, int B, int T, int L, uint8_t* k8,
                                float* k_scale, void* kv, float* kv_scale, hipStream_t stream);
 
+// context-parallel halves (cp.hip; the combine lives beside the split combine)
+hipError_t launch_topk_candidates(const float* scores, const int32_t* idx, int64_t queries, int L,
+                                  int k, int pos_base, float* cand_score, int32_t* cand_idx,
+                                  hipStream_t stream);
+hipError_t launch_topk_merge(const float* cand_score, const int32_t* cand_idx, int G,
+                             int64_t queries, int k_in, int k, int32_t* idx, hipStream_t stream);
+hipError_t launch_idx_localize(const int32_t* idx, int64_t queries, int k, int lo, int hi,
+                               int32_t* local, hipStream_t stream);
+hipError_t launch_lse_combine(const uint16_t* part_out, const float* part_lse, int G,
+                              int64_t queries, uint16_t* out, float* lse, hipStream_t stream);
+
 }  // namespace lcs

@@ -1106,7 +1106,11 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
 }
 
 // out[q][h][:] = sum_s w_s * o_s / sum_s w_s with w_s = 2^(lse_s - max lse)
-// (log2 domain). 256 threads per workgroup = G split groups x 256/G columns
+// (log2 domain; partial lse values are multiplied by l_mul on loading: 1 for
+// the attention kernels' own log2 partials, log2(e) for natural-log lse).
+// Partial s of query q sits at part_o + q * o_q + s * o_s (elements) and
+// part_lse + q * l_q + s * l_s: query-major for the splits of one launch,
+// shard-major for outputs gathered from several devices. 256 threads per workgroup = G split groups x 256/G columns
 // of four output elements; a workgroup covers 1024/G consecutive elements of
 // a query's [64 heads][512] output, so a query spreads over 32 G workgroups.
 // Group g folds splits g, g + G, g + 2G, ... with a running maximum, the
@@ -1117,7 +1121,9 @@ constexpr int kCombBatch = 8;
 template <int G>
 __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
-                                                      int splits, uint16_t* __restrict__ out,
+                                                      int splits, int64_t o_q, int64_t o_s,
+                                                      int64_t l_q, int64_t l_s, float l_mul,
+                                                      uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
   constexpr int kCols = 256 / G;
   __shared__ v4f s_acc[G > 1 ? G - 1 : 1][kCols];
@@ -1127,8 +1133,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
   const int64_t per_split = (int64_t)kAttHeads * kLatent;
   const int e = blockIdx.x * (4 * kCols) + 4 * col;  // element within a split's output
   const int head = e / kLatent;
-  const uint16_t* base = part_o + (int64_t)qi * splits * per_split + e;
-  const float* lbase = part_lse + (int64_t)qi * splits * kAttHeads + head;
+  const uint16_t* base = part_o + (int64_t)qi * o_q + e;
+  const float* lbase = part_lse + (int64_t)qi * l_q + head;
   float m = -INFINITY, wsum = 0.f;
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = grp; s0 < splits; s0 += G * kCombBatch) {
@@ -1141,8 +1147,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
       o[j] = v4f{0.f, 0.f, 0.f, 0.f};
       if (j < nb) {
         const int64_t sp = s0 + G * j;
-        l[j] = lbase[sp * kAttHeads];
-        const v2i x = *(const v2i*)(base + sp * per_split);  // four bf16
+        l[j] = lbase[sp * l_s] * l_mul;
+        const v2i x = *(const v2i*)(base + sp * o_s);  // four bf16
         o[j] = v4f{__uint_as_float((uint32_t)x[0] << 16), __uint_as_float((uint32_t)x[0] & 0xFFFF0000u),
                    __uint_as_float((uint32_t)x[1] << 16), __uint_as_float((uint32_t)x[1] & 0xFFFF0000u)};
       }
@@ -1238,11 +1244,28 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
     e = launch_kernel(sparse_mla_kernel<false>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx,
                       T, L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
   if (e != hipSuccess || p.splits <= 1) return e;
+  const int64_t per = (int64_t)kAttHeads * kLatent;
   if (p.splits <= kCombBatch)
     return launch_kernel(combine_kernel<1>, dim3(32, (unsigned)queries), dim3(256), 0, stream,
-                         part_o, part_lse, p.splits, out, lse);
+                         part_o, part_lse, p.splits, p.splits * per, per,
+                         (int64_t)p.splits * kAttHeads, (int64_t)kAttHeads, 1.0f, out, lse);
   return launch_kernel(combine_kernel<4>, dim3(32 * 4, (unsigned)queries), dim3(256), 0, stream,
-                       part_o, part_lse, p.splits, out, lse);
+                       part_o, part_lse, p.splits, p.splits * per, per,
+                       (int64_t)p.splits * kAttHeads, (int64_t)kAttHeads, 1.0f, out, lse);
+}
+
+hipError_t launch_lse_combine(const uint16_t* part_out, const float* part_lse, int G,
+                              int64_t queries, uint16_t* out, float* lse, hipStream_t stream) {
+  // shard-major [G][queries]; natural-log lse
+  const int64_t per = (int64_t)kAttHeads * kLatent;
+  if (queries == 0) return hipSuccess;
+  if (G <= kCombBatch)
+    return launch_kernel(combine_kernel<1>, dim3(32, (unsigned)queries), dim3(256), 0, stream,
+                         part_out, part_lse, G, per, queries * per, (int64_t)kAttHeads,
+                         queries * kAttHeads, kLog2e, out, lse);
+  return launch_kernel(combine_kernel<4>, dim3(32 * 4, (unsigned)queries), dim3(256), 0, stream,
+                       part_out, part_lse, G, per, queries * per, (int64_t)kAttHeads,
+                       queries * kAttHeads, kLog2e, out, lse);
 }
 
 }  // namespace lcs

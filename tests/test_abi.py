@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_function():
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -113,6 +113,28 @@ def test_cache_append_validation():
     assert f(P, None, 0, P, 1, 1, 8, P, P, P, None, None) == SHAPE  # kv without kv_new
     assert f(P, P, 0, P, 1, 0, 8, P, P, P, None, None) == SHAPE
     assert f(P, P, 0, P + 4, 1, 1, 8, P, P, P, None, None) == SHAPE
+
+
+def test_context_parallel_validation():
+    cand = _fn("lcs_topk_candidates", [_v, _v] + [_i] * 5 + [_v, _v, _v])
+    assert cand(P, P, 1, 1, 100, 64, 0, P, None, None) == NULL
+    assert cand(P, P, 1, 1, 100, 0, 0, P, P, None) == UNSUP
+    assert cand(P, P, 1, 1, 100, 64, -1, P, P, None) == SHAPE
+    assert cand(P, P, 1, 1, 100, 64, 0x7FFFFFFF - 99, P, P, None) == SHAPE
+    merge = _fn("lcs_topk_merge", [_v, _v] + [_i] * 5 + [_v, _v])
+    assert merge(P, P, 17, 1, 1, 2048, 2048, P, None) == UNSUP and b"32768" in last()
+    assert merge(P, P, 0, 1, 1, 2048, 2048, P, None) == SHAPE
+    assert merge(P, P, 2, 1, 1, 2048, 4096, P, None) == UNSUP
+    assert merge(P, None, 2, 1, 1, 2048, 2048, P, None) == NULL
+    loc = _fn("lcs_idx_localize", [_v] + [_i] * 5 + [_v, _v])
+    assert loc(P, 1, 1, 64, 10, 5, P + 256, None) == SHAPE
+    assert loc(P, 1, 1, 64, 0, 5, P, None) == SHAPE and b"alias" in last()
+    assert loc(P, 0, 1, 64, 0, 5, P + 256, None) == SHAPE
+    comb = _fn("lcs_lse_combine", [_v, _v] + [_i] * 3 + [_v, _v, _v])
+    assert comb(P, P, 0, 1, 1, P, None, None) == SHAPE
+    assert comb(P, P, 1025, 1, 1, P, None, None) == SHAPE
+    assert comb(P, P, 2, 1, 1, None, None, None) == NULL
+    assert comb(P, P, 2, 1, 1, P, P + 4, None) == SHAPE
 
 
 def test_schedules_and_counts():

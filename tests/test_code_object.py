@@ -57,7 +57,8 @@ def test_no_kernel_uses_scratch(tmp_path):
     names = " ".join(n for n, _ in ks)
     for expected in ("idx_decode_kernel", "idx_prefill_kernel", "topk_final_kernel",
                      "sparse_mla_b_kernel", "sparse_mla_kernel", "combine_kernel",
-                     "quant_rows_kernel"):
+                     "quant_rows_kernel", "topk_merge_kernel", "candidates_kernel",
+                     "localize_kernel"):
         assert expected in names, expected
     # (SGPR spills go to VGPR lanes, not to memory, and are allowed)
     bad = [(n, f) for n, f in ks
