@@ -282,6 +282,53 @@ def time_context_parallel(w, lcs, G=8, n=50):
     return res
 
 
+def time_paged(s, lcs, bs=64, n=20):
+    """One full layer of the workload with its keys and latent rows laid out in
+    pools of bs-row blocks, the blocks in a random order, against the same
+    layer contiguous: mean microseconds per launch of the indexer and of the
+    attention (HIP events on the launch stream around n launches each)."""
+    import numpy as np
+    import torch
+    w = s.w
+    dev = "cuda:0"
+    B, T, L, k = w.B, w.T, w.L, w.k
+    nb_seq = (L + bs - 1) // bs
+    n_blocks = B * nb_seq
+    rs = np.random.default_rng(17)
+    table = rs.permutation(n_blocks).reshape(B, nb_seq).astype(np.int32)
+    pos = np.arange(L)
+    rows = torch.from_numpy((table[:, pos // bs].astype(np.int64) * bs + pos % bs).reshape(-1)).to(dev)
+    paged = lcs.Paged(torch.from_numpy(table).to(dev), bs, n_blocks)
+
+    def pool(x):
+        p = torch.empty((n_blocks * bs,) + tuple(x.shape[2:]), dtype=x.dtype, device=dev)
+        p[rows] = x.reshape((-1,) + tuple(x.shape[2:]))
+        return p
+    d = s.layers(0, False)[0]
+    k8p, ksp = pool(d["k8"]), pool(d["k_scale"])
+    kvp = pool(d["kv"])
+    kvsp = pool(d["kv_scale"]) if d["kv_scale"] is not None else None
+    idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+    lcs.idx_score(d["q8"], d["q_scale"], d["w"], d["k8"], d["k_scale"], s.vis, s.scores)
+    lcs.topk_select(s.scores, s.vis, k, idx, s.ws_topk)
+    out = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=dev)
+    calls = {
+        "idx_score": lambda: lcs.idx_score(d["q8"], d["q_scale"], d["w"], d["k8"], d["k_scale"],
+                                           s.vis, s.scores),
+        "idx_score_paged": lambda: lcs.idx_score_paged(d["q8"], d["q_scale"], d["w"], k8p, ksp,
+                                                       paged, s.vis, L, s.scores),
+        "sparse_mla_attn": lambda: lcs.sparse_mla_attn(d["q"], d["kv"], d["kv_scale"], idx,
+                                                       w.sm_scale, out, None, s.ws_attn),
+        "sparse_mla_attn_paged": lambda: lcs.sparse_mla_attn_paged(
+            d["q"], kvp, kvsp, paged, idx, L, w.sm_scale, out, None, s.ws_attn),
+    }
+    res = {}
+    for name, fn in calls.items():
+        res[name] = round(timed(lambda m: [fn() for _ in range(m)], n, 3) * 1000.0, 2)
+    del k8p, ksp, kvp, kvsp
+    return res
+
+
 def step_bytes(w, off):
     """algorithmic HBM bytes of one step (keys+scales+queries, gathered rows and
     attention I/O); intermediates (scores, selections) are not counted"""
@@ -416,6 +463,9 @@ def main():
                                "bytes_per_launch": ap_bytes,
                                "achieved_GBs": round(ap_bytes / (ap_us * 1e-6) / 1e9, 1),
                                "note": "keys + latent rows of one layer; not part of the step"}
+        if not w.mtp_steps:
+            res["paged"] = {"block_size": 64, "note": "one full layer, blocks in random order; "
+                            "not part of the step", "us_per_launch": time_paged(s, lcs)}
         if w.T < IDX_PREFILL_MIN_T:
             cp = time_context_parallel(w, lcs)
             res["context_parallel"] = {

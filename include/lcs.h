@@ -264,6 +264,50 @@ lcs_status lcs_idx_localize(const int32_t* idx, int32_t B, int32_t T, int32_t k,
 lcs_status lcs_lse_combine(const uint16_t* part_out, const float* part_lse, int32_t G, int32_t B,
                            int32_t T, uint16_t* out, float* lse, hipStream_t stream);
 
+/* Paged KV. The pages credit finer-grained management of KV-cache memory
+ * (LayerSplit) with raising the cache's capacity (section "推理优化" of
+ * "GLM-5.2 — 1M上下文开放权重的长程任务旗舰"; the agents-report article makes
+ * the same point) and do not describe it; the layout here is a reading: caches live in pools of fixed-size blocks, and each sequence maps
+ * its position blocks to pool blocks through a table. Position p of sequence
+ * b is pool row block_table[b * max_blocks + p / block_size] * block_size +
+ * p % block_size; one table serves the key pool and the latent pool of a
+ * layer. Pools: k8 [n_blocks][block_size][128] E4M3 + k_scale
+ * [n_blocks][block_size] fp32; kv [n_blocks][block_size][576] (bf16, or E4M3
+ * + kv_scale [n_blocks][block_size]). Results equal those of the contiguous
+ * calls on the same logical cache, bit for bit. */
+typedef struct {
+  const int32_t* block_table; /* [B][max_blocks] int32, DEVICE memory */
+  int32_t max_blocks;         /* table entries per sequence; L <= max_blocks * block_size */
+  int32_t block_size;         /* rows per block: a power of two >= 64 */
+  int32_t n_blocks;           /* blocks in each pool; n_blocks * block_size < 2^31.
+                               * Table entries are clamped to [0, n_blocks) on the
+                               * device, so a bad entry reads or writes a wrong row
+                               * of the pool, never memory outside it. */
+} lcs_paged;
+
+/* lcs_idx_score over paged keys (paged is a HOST pointer). */
+lcs_status lcs_idx_score_paged(const uint8_t* q8, const float* q_scale, const float* w,
+                               const uint8_t* k8_pool, const float* k_scale_pool,
+                               const lcs_paged* paged, const int32_t* vis_len, int32_t B,
+                               int32_t T, int32_t L, float* scores, hipStream_t stream);
+
+/* lcs_sparse_mla_attn over a paged latent cache; workspace as
+ * lcs_attn_workspace_bytes(B, T, k). Pools may exceed 4 GB. */
+lcs_status lcs_sparse_mla_attn_paged(const uint16_t* q, const void* kv_pool,
+                                     lcs_kv_dtype kv_dtype, const float* kv_scale_pool,
+                                     const lcs_paged* paged, const int32_t* idx, int32_t B,
+                                     int32_t T, int32_t L, int32_t k, float sm_scale,
+                                     uint16_t* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/* lcs_cache_append into paged caches: token (b, t) goes to the pool row of
+ * position pos[b,t] (positions outside [0, L) are skipped). */
+lcs_status lcs_cache_append_paged(const uint16_t* k_new, const uint16_t* kv_new,
+                                  lcs_kv_dtype kv_dtype, const int32_t* pos, int32_t B, int32_t T,
+                                  int32_t L, const lcs_paged* paged, uint8_t* k8_pool,
+                                  float* k_scale_pool, void* kv_pool, float* kv_scale_pool,
+                                  hipStream_t stream);
+
 /* Static description of a status code. */
 const char* lcs_status_string(lcs_status s);
 /* Thread-local detail of this thread's last failed call ("" if none). */

@@ -17,7 +17,7 @@ __all__ = [
     "sparse_mla_attn", "count_full_layers", "indexshare_workspace_bytes", "indexshare_forward",
     "SCHED_GROUP4", "SCHED_GLM52", "SCHED_ALL_FULL", "SCHED_MASK", "KV_BF16", "KV_FP8_E4M3",
     "LIB_PATH", "quantize_e4m3", "cache_append", "topk_candidates", "topk_merge", "idx_localize",
-    "lse_combine",
+    "lse_combine", "Paged", "idx_score_paged", "sparse_mla_attn_paged", "cache_append_paged",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblcs.so")
@@ -33,6 +33,25 @@ _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _sz = ctypes.c_size_t
 _f32 = ctypes.c_float
+
+
+class _PagedC(ctypes.Structure):
+    _fields_ = [("block_table", _p), ("max_blocks", _i32), ("block_size", _i32),
+                ("n_blocks", _i32)]
+
+
+class Paged:
+    """A paged cache layout: block_table [B, max_blocks] int32 device tensor mapping each
+    sequence's position blocks to pool blocks of block_size rows; n_blocks pool blocks."""
+
+    def __init__(self, block_table, block_size, n_blocks):
+        self.block_table = block_table
+        self.block_size = int(block_size)
+        self.n_blocks = int(n_blocks)
+
+    def _c(self):
+        return ctypes.byref(_PagedC(self.block_table.data_ptr(), self.block_table.shape[1],
+                                    self.block_size, self.n_blocks))
 
 
 class _Layer(ctypes.Structure):
@@ -65,6 +84,11 @@ _c_cand = _sig("lcs_topk_candidates", ctypes.c_int, [_p, _p] + [_i32] * 5 + [_p,
 _c_merge = _sig("lcs_topk_merge", ctypes.c_int, [_p, _p] + [_i32] * 5 + [_p, _p])
 _c_local = _sig("lcs_idx_localize", ctypes.c_int, [_p] + [_i32] * 5 + [_p, _p])
 _c_comb = _sig("lcs_lse_combine", ctypes.c_int, [_p, _p] + [_i32] * 3 + [_p, _p, _p])
+_c_idx_paged = _sig("lcs_idx_score_paged", ctypes.c_int, [_p] * 6 + [_p] + [_i32] * 3 + [_p, _p])
+_c_attn_paged = _sig("lcs_sparse_mla_attn_paged", ctypes.c_int,
+                     [_p, _p, ctypes.c_int, _p, _p, _p] + [_i32] * 4 + [_f32, _p, _p, _p, _sz, _p])
+_c_append_paged = _sig("lcs_cache_append_paged", ctypes.c_int,
+                       [_p, _p, ctypes.c_int, _p] + [_i32] * 3 + [_p] * 6)
 _c_status = _sig("lcs_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_last = _sig("lcs_last_error", ctypes.c_char_p, [])
 
@@ -219,3 +243,35 @@ def lse_combine(part_out, part_lse, out, lse=None, stream=None):
     G, B, T = part_out.shape[:3]
     _check(_c_comb(_ptr(part_out), _ptr(part_lse), G, B, T, _ptr(out), _ptr(lse),
                    _stream(stream)))
+
+
+def idx_score_paged(q8, q_scale, w, k8_pool, k_scale_pool, paged, vis_len, L, scores,
+                    stream=None):
+    """lcs_idx_score over the key pools k8_pool [n_blocks, bs, 128] / k_scale_pool
+    [n_blocks, bs] of a Paged layout; scores [B, T, L]."""
+    B, T = q8.shape[0], q8.shape[1]
+    _check(_c_idx_paged(_ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8_pool), _ptr(k_scale_pool),
+                        paged._c(), _ptr(vis_len), B, T, L, _ptr(scores), _stream(stream)))
+
+
+def sparse_mla_attn_paged(q, kv_pool, kv_scale_pool, paged, idx, L, sm_scale, out, lse=None,
+                          workspace=None, stream=None):
+    """lcs_sparse_mla_attn over the latent pool kv_pool [n_blocks, bs, 576] (bf16, or uint8
+    E4M3 codes with kv_scale_pool [n_blocks, bs]) of a Paged layout."""
+    B, T = q.shape[0], q.shape[1]
+    k = idx.shape[-1]
+    _check(_c_attn_paged(_ptr(q), _ptr(kv_pool), _kv_dtype(kv_pool), _ptr(kv_scale_pool),
+                         paged._c(), _ptr(idx), B, T, L, k, float(sm_scale), _ptr(out), _ptr(lse),
+                         _ptr(workspace),
+                         0 if workspace is None else workspace.numel() * workspace.element_size(),
+                         _stream(stream)))
+
+
+def cache_append_paged(pos, L, paged, k_new=None, k8_pool=None, k_scale_pool=None, kv_new=None,
+                       kv_pool=None, kv_scale_pool=None, stream=None):
+    """lcs_cache_append into the pools of a Paged layout (positions outside [0, L) skipped)."""
+    B, T = pos.shape
+    kd = _kv_dtype(kv_pool) if kv_pool is not None else KV_BF16
+    _check(_c_append_paged(_ptr(k_new), _ptr(kv_new), kd, _ptr(pos), B, T, L, paged._c(),
+                           _ptr(k8_pool), _ptr(k_scale_pool), _ptr(kv_pool), _ptr(kv_scale_pool),
+                           _stream(stream)))

@@ -32,7 +32,9 @@ constexpr int kRows576PerBlock = 4;   // 4 waves x 1 row
 // One set of rows to process. Row r of src goes to destination row
 //   r                              (dst_pos == nullptr), or
 //   (r / T) * L + dst_pos[r]       (cache append; skipped when dst_pos[r]
-//                                   is outside [0, L)).
+//                                   is outside [0, L)), or, with a block
+//   table (paged caches), pool row (blk << lbs) + (p & (2^lbs - 1)) with
+//   blk = btab[(r / T) * max_blocks + (p >> lbs)] clamped to the pool.
 // codes != nullptr: quantise into codes/scales; else copy the bf16 row to copy
 // (576-wide rows only: a bf16 latent cache takes the new rows as they are).
 struct RowJob {
@@ -44,6 +46,8 @@ struct RowJob {
   uint8_t* codes;
   float* scales;
   uint16_t* copy;
+  const int32_t* btab;
+  int max_blocks, lbs, n_blocks;
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -80,7 +84,9 @@ __device__ __forceinline__ int64_t dst_row(const RowJob& j, int64_t r, bool& val
   }
   const int p = j.dst_pos[r];
   valid = p >= 0 && p < j.L;
-  return (r / j.T) * (int64_t)j.L + p;
+  if (!j.btab) return (r / j.T) * (int64_t)j.L + p;
+  const int blk = valid ? j.btab[(r / j.T) * (int64_t)j.max_blocks + (p >> j.lbs)] : 0;
+  return ((int64_t)min(max(blk, 0), j.n_blocks - 1) << j.lbs) + (p & ((1 << j.lbs) - 1));
 }
 
 // 8 values -> 8 codes packed little-endian into two words
@@ -177,20 +183,26 @@ hipError_t launch_jobs(const RowJob& j128, const RowJob& j576, hipStream_t strea
 hipError_t launch_quantize_e4m3(const uint16_t* x, int64_t rows, int D, uint8_t* codes,
                                 float* scales, hipStream_t stream) {
   RowJob none{};
-  RowJob job{x, rows, nullptr, 1, 0, codes, scales, nullptr};
+  RowJob job{x, rows, nullptr, 1, 0, codes, scales, nullptr, nullptr, 0, 0, 0};
   return D == kIdxDim ? launch_jobs(job, none, stream) : launch_jobs(none, job, stream);
 }
 
 hipError_t launch_cache_append(const uint16_t* k_new, const uint16_t* kv_new, bool kv_fp8,
                                const int32_t* pos, int B, int T, int L, uint8_t* k8,
-                               float* k_scale, void* kv, float* kv_scale, hipStream_t stream) {
+                               float* k_scale, void* kv, float* kv_scale,
+                               const int32_t* block_table, int max_blocks, int lbs, int n_blocks,
+                               hipStream_t stream) {
   const int64_t tokens = (int64_t)B * T;
   RowJob keys{};
   RowJob lat{};
-  if (k_new) keys = RowJob{k_new, tokens, pos, T, L, k8, k_scale, nullptr};
+  if (k_new)
+    keys = RowJob{k_new, tokens, pos, T, L, k8, k_scale, nullptr, block_table, max_blocks, lbs,
+                  n_blocks};
   if (kv_new)
-    lat = kv_fp8 ? RowJob{kv_new, tokens, pos, T, L, (uint8_t*)kv, kv_scale, nullptr}
-                 : RowJob{kv_new, tokens, pos, T, L, nullptr, nullptr, (uint16_t*)kv};
+    lat = kv_fp8 ? RowJob{kv_new, tokens, pos, T, L, (uint8_t*)kv, kv_scale, nullptr, block_table,
+                          max_blocks, lbs, n_blocks}
+                 : RowJob{kv_new, tokens, pos, T, L, nullptr, nullptr, (uint16_t*)kv, block_table,
+                          max_blocks, lbs, n_blocks};
   return launch_jobs(keys, lat, stream);
 }
 

@@ -153,6 +153,27 @@ lcs_status validate_append(const uint16_t* k_new, const uint16_t* kv_new, int kv
   return LCS_OK;
 }
 
+// A paged layout: a table of int32 pool blocks, power-of-two blocks of at
+// least 64 rows, L within the table, pool rows addressable in int32.
+lcs_status validate_paged(const lcs_paged* pg, int32_t L, int* lbs) {
+  if (!pg) return fail(LCS_ERR_NULL, "paged layout is NULL");
+  REQUIRE(pg->block_table, "block_table");
+  const int32_t bs = pg->block_size;
+  if (bs < 64 || (bs & (bs - 1)) != 0)
+    return fail(LCS_ERR_UNSUPPORTED, "block_size = %d is not a power of two >= 64", bs);
+  if (pg->max_blocks <= 0 || pg->n_blocks <= 0)
+    return fail(LCS_ERR_SHAPE, "max_blocks and n_blocks must be positive");
+  if ((int64_t)pg->max_blocks * bs < L)
+    return fail(LCS_ERR_SHAPE, "L = %d exceeds max_blocks * block_size = %lld", L,
+                (long long)pg->max_blocks * bs);
+  if ((int64_t)pg->n_blocks * bs > 0x7FFFFFFF)
+    return fail(LCS_ERR_SHAPE, "n_blocks * block_size must stay below 2^31 rows");
+  int l = 0;
+  while ((1 << l) < bs) ++l;
+  *lbs = l;
+  return LCS_OK;
+}
+
 bool is_full_layer(lcs_sched sched, int32_t l, const uint8_t* mask) {
   switch (sched) {
     case LCS_SCHED_GROUP4:
@@ -248,7 +269,7 @@ lcs_status lcs_cache_append(const uint16_t* k_new, const uint16_t* kv_new, lcs_k
                             float* k_scale, void* kv, float* kv_scale, hipStream_t stream) {
   TRY(validate_append(k_new, kv_new, (int)kv_dtype, pos, B, T, L, k8, k_scale, kv, kv_scale));
   TRY(hip_status(lcs::launch_cache_append(k_new, kv_new, kv_dtype == LCS_KV_FP8_E4M3, pos, B, T,
-                                          L, k8, k_scale, kv, kv_scale, stream),
+                                          L, k8, k_scale, kv, kv_scale, nullptr, 0, 0, 0, stream),
                  "cache_append launch"));
   return ok();
 }
@@ -312,6 +333,55 @@ lcs_status lcs_lse_combine(const uint16_t* part_out, const float* part_lse, int3
   TRY(check_dims(B, T, 1));
   TRY(hip_status(lcs::launch_lse_combine(part_out, part_lse, G, (int64_t)B * T, out, lse, stream),
                  "lse_combine launch"));
+  return ok();
+}
+
+lcs_status lcs_idx_score_paged(const uint8_t* q8, const float* q_scale, const float* w,
+                               const uint8_t* k8_pool, const float* k_scale_pool,
+                               const lcs_paged* paged, const int32_t* vis_len, int32_t B,
+                               int32_t T, int32_t L, float* scores, hipStream_t stream) {
+  TRY(validate_idx_score(q8, q_scale, w, k8_pool, k_scale_pool, vis_len, B, T, L, scores));
+  int lbs = 0;
+  TRY(validate_paged(paged, L, &lbs));
+  TRY(hip_status(lcs::launch_idx_score_paged(q8, q_scale, w, k8_pool, k_scale_pool,
+                                             paged->block_table, paged->max_blocks, lbs,
+                                             paged->n_blocks, vis_len, B, T, L, scores, stream),
+                 "idx_score launch"));
+  return ok();
+}
+
+lcs_status lcs_sparse_mla_attn_paged(const uint16_t* q, const void* kv_pool,
+                                     lcs_kv_dtype kv_dtype, const float* kv_scale_pool,
+                                     const lcs_paged* paged, const int32_t* idx, int32_t B,
+                                     int32_t T, int32_t L, int32_t k, float sm_scale,
+                                     uint16_t* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  TRY(validate_attn(q, kv_pool, (int)kv_dtype, kv_scale_pool, idx, B, T, L, k, sm_scale, out, lse,
+                    workspace, workspace_bytes));
+  int lbs = 0;
+  TRY(validate_paged(paged, L, &lbs));
+  TRY(hip_status(lcs::launch_sparse_mla_paged(q, kv_pool, kv_dtype == LCS_KV_FP8_E4M3,
+                                              kv_scale_pool, paged->block_table,
+                                              paged->max_blocks, lbs, paged->n_blocks, idx, B, T,
+                                              L, k, sm_scale, out, lse, workspace, stream),
+                 "sparse_mla launch"));
+  return ok();
+}
+
+lcs_status lcs_cache_append_paged(const uint16_t* k_new, const uint16_t* kv_new,
+                                  lcs_kv_dtype kv_dtype, const int32_t* pos, int32_t B, int32_t T,
+                                  int32_t L, const lcs_paged* paged, uint8_t* k8_pool,
+                                  float* k_scale_pool, void* kv_pool, float* kv_scale_pool,
+                                  hipStream_t stream) {
+  TRY(validate_append(k_new, kv_new, (int)kv_dtype, pos, B, T, L, k8_pool, k_scale_pool, kv_pool,
+                      kv_scale_pool));
+  int lbs = 0;
+  TRY(validate_paged(paged, L, &lbs));
+  TRY(hip_status(lcs::launch_cache_append(k_new, kv_new, kv_dtype == LCS_KV_FP8_E4M3, pos, B, T, L,
+                                          k8_pool, k_scale_pool, kv_pool, kv_scale_pool,
+                                          paged->block_table, paged->max_blocks, lbs,
+                                          paged->n_blocks, stream),
+                 "cache_append launch"));
   return ok();
 }
 

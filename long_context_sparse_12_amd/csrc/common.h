@@ -92,6 +92,12 @@ hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float
                             const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
                             int B, int T, int L, float* scores, hipStream_t stream);
 
+hipError_t launch_idx_score_paged(const uint8_t* q8, const float* q_scale, const float* w,
+                                  const uint8_t* k8, const float* k_scale,
+                                  const int32_t* block_table, int max_blocks, int lbs,
+                                  int n_blocks, const int32_t* vis_len, int B, int T, int L,
+                                  float* scores, hipStream_t stream);
+
 size_t topk_workspace_bytes(int64_t rows, int L, int k);
 hipError_t launch_topk(const float* scores, const int32_t* vis_len, int rows, int L, int k,
                        int32_t* idx, void* workspace, hipStream_t stream);
@@ -102,12 +108,25 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
                              int k, float sm_scale, uint16_t* out, float* lse,
                              void* workspace, hipStream_t stream);
 
+// paged KV: kv/kv_scale are pools of 2^lbs-row blocks, block_table [B][max_blocks]
+hipError_t launch_sparse_mla_paged(const uint16_t* q, const void* kv, bool kv_fp8,
+                                   const float* kv_scale, const int32_t* block_table,
+                                   int max_blocks, int lbs, int n_blocks, const int32_t* idx,
+                                   int B, int T, int L, int k, float sm_scale, uint16_t* out,
+                                   float* lse, void* workspace, hipStream_t stream);
+// merge of `splits` query-major attention partials (the attention's own workspace)
+hipError_t launch_split_combine(const uint16_t* part_o, const float* part_lse, int splits,
+                                int64_t queries, uint16_t* out, float* lse, hipStream_t stream);
+
 // D = 128 or 576
 hipError_t launch_quantize_e4m3(const uint16_t* x, int64_t rows, int D, uint8_t* codes,
                                 float* scales, hipStream_t stream);
+// block_table == nullptr: contiguous caches [B][L]; else pools of 2^lbs-row blocks
 hipError_t launch_cache_append(const uint16_t* k_new, const uint16_t* kv_new, bool kv_fp8,
                                const int32_t* pos, int B, int T, int L, uint8_t* k8,
-                               float* k_scale, void* kv, float* kv_scale, hipStream_t stream);
+                               float* k_scale, void* kv, float* kv_scale,
+                               const int32_t* block_table, int max_blocks, int lbs, int n_blocks,
+                               hipStream_t stream);
 
 // context-parallel halves (cp.hip; the combine lives beside the split combine)
 hipError_t launch_topk_candidates(const float* scores, const int32_t* idx, int64_t queries, int L,

@@ -72,12 +72,20 @@ __device__ __forceinline__ float sum_pair(float x, float y) {
 // result holds, in lane l, key l&31 of the block and heads 8(i/4) + 4(l>>5) +
 // (i&3) for i = 0..15, so the head sum is 16 in-lane FMAs and one exchange
 // between the lane halves.
-template <int TQ>
+//
+// Paged keys (PAGED): k8 and k_scale are pools of blocks of 2^lbs >= 64 rows
+// and block_table [B][max_blocks] maps a sequence's blocks to pool blocks. A
+// 64-key tile starts at a multiple of 64, so it lies in one block; the
+// workgroup's slice of the table (at most 65 entries) sits in LDS.
+constexpr int kMaxWgBlocks = LCS_IDX_MAX_ITERS * kWaves * kSuper / 64 + 1;
+template <int TQ, bool PAGED>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 1 ? 4 : 2))) idx_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const int32_t* __restrict__ vis_len, int T,
-    int t0, int L, int keys_per_wg, float* __restrict__ scores) {
+    int t0, int L, int keys_per_wg, float* __restrict__ scores,
+    const int32_t* __restrict__ block_table, int max_blocks, int lbs, int n_blocks) {
+  __shared__ int32_t s_blk[PAGED ? kMaxWgBlocks : 1];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -103,6 +111,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
   const int64_t key_base_b = (int64_t)b * L;
   const int wg_begin = blockIdx.x * keys_per_wg;
   const int wg_end = min(L, wg_begin + keys_per_wg);
+  const int blk0 = wg_begin >> lbs;
+  if (PAGED) {
+    const int nb = ((wg_end - 1) >> lbs) - blk0 + 1;
+    if ((int)threadIdx.x < nb)
+      s_blk[threadIdx.x] =
+          min(max(block_table[(int64_t)b * max_blocks + blk0 + threadIdx.x], 0), n_blocks - 1);
+    __syncthreads();
+  }
 
   int base = wg_begin + wave * kSuper;
   if (base >= wg_end) return;
@@ -110,6 +126,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
   // keys [tile_base + 32 blk + ln], K halves 0 and 1, and the scale of key
   // tile_base + lane
   auto load_tile = [&](int tile_base, v8i (&bv)[4], float& ks) {
+    if (PAGED) {
+      // the tile's pool rows: one block, so the keys past L are pool rows too
+      const int64_t prow = ((int64_t)s_blk[(tile_base >> lbs) - blk0] << lbs) +
+                           (tile_base & ((1 << lbs) - 1));
+      ks = k_scale[prow + lane];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const uint8_t* row = k8 + (prow + 32 * blk + ln) * kIdxDim + 32 * hh;
+        bv[2 * blk] = *(const v8i*)(row);
+        bv[2 * blk + 1] = *(const v8i*)(row + 64);
+      }
+      return;
+    }
     const int sk = tile_base + lane;
     ks = k_scale[key_base_b + (sk < L ? sk : L - 1)];
 #pragma unroll
@@ -191,11 +220,13 @@ constexpr int kPfWBytes = kPfChunk * kIdxHeads * 4;        // 1024
 constexpr int kPfBufBytes = kPfQBytes + kPfWBytes;
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 (gfx9): 32-bit data format
 
+template <bool PAGED>
 __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const int32_t* __restrict__ vis_len, int T, int L,
-    int queries_per_wg, float* __restrict__ scores) {
+    int queries_per_wg, float* __restrict__ scores, const int32_t* __restrict__ block_table,
+    int max_blocks, int lbs, int n_blocks) {
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[2][kPfBufBytes];
 
   const int b = blockIdx.z;
@@ -210,23 +241,25 @@ __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
   const int64_t key_base_b = (int64_t)b * L;
   const int kw0 = blockIdx.x * kPfKeysPerWg + wave * kPfKeysPerWave;
 
+  // row of a key (clamped to L - 1): b * L + key, or its pool row (paged)
+  auto key_row = [&](int key) -> int64_t {
+    key = key < L ? key : L - 1;
+    if (!PAGED) return key_base_b + key;
+    const int blk = min(max(block_table[(int64_t)b * max_blocks + (key >> lbs)], 0), n_blocks - 1);
+    return ((int64_t)blk << lbs) + (key & ((1 << lbs) - 1));
+  };
   // this wave's keys: block kb holds keys kw0 + 32 kb + (lane & 31)
   v8i kreg[kPfKB][2];
 #pragma unroll
   for (int kb = 0; kb < kPfKB; ++kb) {
-    int key = kw0 + 32 * kb + ln;
-    key = key < L ? key : L - 1;
-    const uint8_t* row = k8 + (key_base_b + key) * kIdxDim + 32 * hh;
+    const uint8_t* row = k8 + key_row(kw0 + 32 * kb + ln) * kIdxDim + 32 * hh;
     kreg[kb][0] = *(const v8i*)(row);
     kreg[kb][1] = *(const v8i*)(row + 64);
   }
   // scales of the keys this lane stores: kw0 + 64 c + lane
   float ks[kPfKB / 2];
 #pragma unroll
-  for (int c = 0; c < kPfKB / 2; ++c) {
-    const int key = kw0 + 64 * c + lane;
-    ks[c] = k_scale[key_base_b + (key < L ? key : L - 1)];
-  }
+  for (int c = 0; c < kPfKB / 2; ++c) ks[c] = k_scale[key_row(kw0 + 64 * c + lane)];
   // Wait for the keys here: left pending, the compiler would wait with
   // vmcnt(0) at their first use inside the chunk loop, which also waits for
   // the next chunk's loads in flight.
@@ -368,9 +401,13 @@ __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
 
 }  // namespace
 
-hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
-                            const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
-                            int B, int T, int L, float* scores, hipStream_t stream) {
+namespace {
+
+template <bool PAGED>
+hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float* w,
+                           const uint8_t* k8, const float* k_scale, const int32_t* vis_len, int B,
+                           int T, int L, float* scores, const int32_t* btab, int max_blocks,
+                           int lbs, int n_blocks, hipStream_t stream) {
   if (T >= LCS_IDX_PREFILL_MIN_T) {
     // workgroups: key blocks of 1024 x query ranges x batch, the query ranges
     // (multiples of the 8-query chunk) sized for about 4 workgroups per CU
@@ -381,8 +418,9 @@ hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float
     if (want > chunks) want = chunks;
     const int per = (int)((chunks + want - 1) / want) * kPfChunk;
     const int gy = (T + per - 1) / per;
-    return launch_kernel(idx_prefill_kernel, dim3(gx, gy, B), dim3(kPfThreads), 0, stream, q8,
-                         q_scale, w, k8, k_scale, vis_len, T, L, per, scores);
+    return launch_kernel(idx_prefill_kernel<PAGED>, dim3(gx, gy, B), dim3(kPfThreads), 0, stream,
+                         q8, q_scale, w, k8, k_scale, vis_len, T, L, per, scores, btab,
+                         max_blocks, lbs, n_blocks);
   }
   // keys per workgroup: a multiple of 4 waves x 64 keys, sized for enough WGs
   const int64_t total_keys = (int64_t)B * L;
@@ -396,25 +434,47 @@ hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float
     hipError_t e;
     switch (tq) {
       case 1:
-        e = launch_kernel(idx_decode_kernel<1>, grid, dim3(256), 0, stream, q8, q_scale, w, k8,
-                          k_scale, vis_len, T, t0, L, kpw, scores);
+        e = launch_kernel(idx_decode_kernel<1, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w,
+                          k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
+                          n_blocks);
         break;
       case 2:
-        e = launch_kernel(idx_decode_kernel<2>, grid, dim3(256), 0, stream, q8, q_scale, w, k8,
-                          k_scale, vis_len, T, t0, L, kpw, scores);
+        e = launch_kernel(idx_decode_kernel<2, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w,
+                          k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
+                          n_blocks);
         break;
       case 3:
-        e = launch_kernel(idx_decode_kernel<3>, grid, dim3(256), 0, stream, q8, q_scale, w, k8,
-                          k_scale, vis_len, T, t0, L, kpw, scores);
+        e = launch_kernel(idx_decode_kernel<3, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w,
+                          k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
+                          n_blocks);
         break;
       default:
-        e = launch_kernel(idx_decode_kernel<4>, grid, dim3(256), 0, stream, q8, q_scale, w, k8,
-                          k_scale, vis_len, T, t0, L, kpw, scores);
+        e = launch_kernel(idx_decode_kernel<4, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w,
+                          k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
+                          n_blocks);
         break;
     }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
+                            const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
+                            int B, int T, int L, float* scores, hipStream_t stream) {
+  return launch_idx_impl<false>(q8, q_scale, w, k8, k_scale, vis_len, B, T, L, scores, nullptr, 0,
+                                0, 0, stream);
+}
+
+hipError_t launch_idx_score_paged(const uint8_t* q8, const float* q_scale, const float* w,
+                                  const uint8_t* k8, const float* k_scale,
+                                  const int32_t* block_table, int max_blocks, int lbs,
+                                  int n_blocks, const int32_t* vis_len, int B, int T, int L,
+                                  float* scores, hipStream_t stream) {
+  return launch_idx_impl<true>(q8, q_scale, w, k8, k_scale, vis_len, B, T, L, scores, block_table,
+                               max_blocks, lbs, n_blocks, stream);
 }
 
 }  // namespace lcs

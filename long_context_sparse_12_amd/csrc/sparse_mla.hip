@@ -539,8 +539,11 @@ struct AttnB {
   int* flag;        // [2 parity][2 hg]
   int32_t* ring;    // [4 slots][32 rows]  positions of the tiles t with t & 3 = slot
   float* sring;     // [4 slots][32 rows]  FP8 row scales of the same tiles
-  const float* kscale;   // FP8 row scales of this sequence (kv_scale + b * L)
+  const float* kscale;   // FP8 row scales of this sequence (kv_scale + b * L), or
+                         // of the whole pool (paged)
   const int32_t* idx_q;  // this split's selected positions (global memory)
+  const int32_t* btab;   // paged: this sequence's block table row
+  int lbs, nblk;         // paged: log2 rows per block, blocks in the pool
   int n_rows, n_tiles;
   int wave, lane, hg;
 };
@@ -568,6 +571,19 @@ __device__ __forceinline__ void ring_put(const AttnB& c, int tile, int32_t p) {
   if (c.lane < kTileRows) pos_slot(c, tile)[c.lane] = r < c.n_rows ? p : -1;
 }
 
+// Paged KV: a sequence's position p lives in pool block btab[p >> lbs] at row
+// p & (bs - 1). S wave 0 then streams pool rows instead of positions into the
+// ring, one pipeline step later than the positions (the block loads need the
+// positions): positions two steps ahead, blocks one step ahead. Block ids are
+// clamped to the pool; -1 (no row) stays -1.
+__device__ __forceinline__ int32_t load_blk(const AttnB& c, int32_t p) {
+  return c.btab[(p >= 0 ? p : 0) >> c.lbs];
+}
+__device__ __forceinline__ int32_t pool_row(const AttnB& c, int32_t p, int32_t blk) {
+  const int32_t bk = min(max(blk, 0), c.nblk - 1);
+  return p >= 0 ? (bk << c.lbs) | (p & ((1 << c.lbs) - 1)) : -1;
+}
+
 // FP8 KV: the row scales follow the positions one step later (their loads
 // need the positions): tile t's scales go into slot t & 3 of the scale ring
 // in step t-3 and are read by the S waves in step t-1.
@@ -584,6 +600,8 @@ struct SWave {
   float m_run, l_run;
   int32_t pn;  // S wave 0: positions of the next tile to enter the ring
   float sn;    // S wave 0, FP8: scales of the next tile to enter the scale ring
+  int32_t bn;  // S wave 0, paged: pool blocks of the positions pn
+  int32_t pn2; // S wave 0, paged: positions of the tile after pn's
 };
 
 struct PWave {
@@ -593,7 +611,7 @@ struct PWave {
 
 struct GWave {
   int g;                // 0 or 1 (wave-uniform)
-  const uint8_t* kvb;   // this sequence's rows: kv + b * L * (1152 or 576)
+  const uint8_t* kvb;   // this sequence's rows: kv + b * L * (1152 or 576); paged: the pool
   int dma_row[kDmaPerB];  // row inside the tile of each gather
   int dma_off[kDmaPerB];  // byte offset inside the row (swizzled granule)
 };
@@ -607,7 +625,7 @@ struct GWave {
 constexpr int kFp8Per = kTileRows * (kKvDim / 16) / (64 * kGatherWaves);  // 9
 struct GWave8 {
   int g;
-  const uint8_t* kvb;     // kv + b * L * 576
+  const uint8_t* kvb;     // kv + b * L * 576; paged: the pool
   int row[kFp8Per];       // tile row of each granule
   int src[kFp8Per];       // byte offset inside the 576-byte row
   int dst[kFp8Per];       // stage byte offset of its first bf16 granule
@@ -617,7 +635,7 @@ struct GWave8 {
 
 __device__ __forceinline__ int stage_off_b(int r, int cg);
 
-template <int B>
+template <int B, bool PAGED>
 __device__ __forceinline__ void fetch_fp8(const AttnB& c, GWave8& w, int tile) {
   const int32_t* slot = pos_slot(c, tile);
   int32_t rows[kFp8Per];
@@ -626,8 +644,10 @@ __device__ __forceinline__ void fetch_fp8(const AttnB& c, GWave8& w, int tile) {
 #pragma unroll
   for (int i = 0; i < kFp8Per; ++i) {
     const uint32_t s = rows[i] >= 0 ? (uint32_t)rows[i] : 0u;  // padding rows load row 0 (masked)
-    // 32-bit offset from the sequence base (the launcher keeps L * 576 < 2^32)
-    w.fr[B][i] = *(const v4i*)(w.kvb + (s * (uint32_t)kKvDim + (uint32_t)w.src[i]));
+    if (PAGED)  // pool row: a 64-bit offset (pools may exceed 4 GB)
+      w.fr[B][i] = *(const v4i*)(w.kvb + ((uint64_t)s * kKvDim + (uint32_t)w.src[i]));
+    else  // 32-bit offset from the sequence base (the launcher keeps L * 576 < 2^32)
+      w.fr[B][i] = *(const v4i*)(w.kvb + (s * (uint32_t)kKvDim + (uint32_t)w.src[i]));
   }
 }
 
@@ -655,7 +675,7 @@ __device__ __forceinline__ void store_fp8(const AttnB& c, const GWave8& w) {
 
 // gathers of `tile` into stage S: gather-wave lane (g, l), gather i covers
 // LDS bytes [1024 (g + 2 i), +1024) of the stage, 16 bytes per lane
-template <int S>
+template <int S, bool PAGED>
 __device__ __forceinline__ void issue_tile_b(const AttnB& c, const GWave& w, int tile) {
   int32_t rows[kDmaPerB];
 #pragma unroll
@@ -663,15 +683,18 @@ __device__ __forceinline__ void issue_tile_b(const AttnB& c, const GWave& w, int
 #pragma unroll
   for (int i = 0; i < kDmaPerB; ++i) {
     const uint32_t s = rows[i] >= 0 ? (uint32_t)rows[i] : 0u;  // padding rows load row 0 (masked)
-    // 32-bit offset from the sequence base (the launcher keeps L * 1152 < 2^32)
-    dma16(w.kvb + (s * (uint32_t)kRowBytes + (uint32_t)w.dma_off[i]),
-          c.st[S] + 1024 * (w.g + kGatherWaves * i));
+    if (PAGED)  // pool row: a 64-bit offset (pools may exceed 4 GB)
+      dma16(w.kvb + ((uint64_t)s * kRowBytes + (uint32_t)w.dma_off[i]),
+            c.st[S] + 1024 * (w.g + kGatherWaves * i));
+    else  // 32-bit offset from the sequence base (the launcher keeps L * 1152 < 2^32)
+      dma16(w.kvb + (s * (uint32_t)kRowBytes + (uint32_t)w.dma_off[i]),
+            c.st[S] + 1024 * (w.g + kGatherWaves * i));
   }
 }
 
 // S^T of one tile and its softmax (S waves); P^T, alpha and the rescale flag
 // go to parity buffer `par`
-template <int S, bool FP8>
+template <int S, bool FP8, bool PAGED>
 __device__ __forceinline__ void s_phase(const AttnB& c, SWave& w, int tile, int par) {
   const int lane = c.lane, ln = lane & 31, h = lane >> 5;
   const uint8_t* tb = c.st[S];
@@ -681,7 +704,9 @@ __device__ __forceinline__ void s_phase(const AttnB& c, SWave& w, int tile, int 
   // A operand of K-step ks: lane holds row (lane&31), dims 16ks + 8h .. +8
   // (granule 2ks + h). The reads run LCS_ATTN_S_AHEAD K-steps ahead of the
   // MFMAs, so the LDS latency is paid once per tile, not once per K-step.
-  constexpr int kAhead = LCS_ATTN_S_AHEAD;
+  // (paged FP8 KV: one K-step less, for the two registers of the block
+  // lookups that S wave 0 carries between steps; 256 VGPRs otherwise spill)
+  constexpr int kAhead = (FP8 && PAGED) ? LCS_ATTN_S_AHEAD - 1 : LCS_ATTN_S_AHEAD;
   v4i a[kAhead];
 #pragma unroll
   for (int ks = 0; ks < kAhead; ++ks) a[ks] = *(const v4i*)(sb[ks & 3] + 128 * (ks >> 2));
@@ -832,10 +857,10 @@ __device__ __forceinline__ void pv_step(const AttnB& c, PWave& w, int j) {
   lds_barrier();
 }
 
-template <int SJ>
+template <int SJ, bool PAGED>
 __device__ __forceinline__ void g_step(const AttnB& c, const GWave& w, int j) {
   const bool more = j + 3 < c.n_tiles;
-  if (more) issue_tile_b<(SJ + 3) % kStagesB>(c, w, j + 3);
+  if (more) issue_tile_b<(SJ + 3) % kStagesB, PAGED>(c, w, j + 3);
   if (j + 2 < c.n_tiles) {
     if (more) wait_vm<kDmaPerB>();
     else wait_vm<0>();
@@ -853,9 +878,9 @@ __device__ __forceinline__ void g_step(const AttnB& c, const GWave& w, int j) {
 // branch; a step past the last tile (j >= n_tiles) skips only the barrier,
 // which the other roles do not have for it (they are done with every stage
 // by then, and the final barrier orders these writes before the epilogue's).
-template <int SJ>
+template <int SJ, bool PAGED>
 __device__ __forceinline__ void g_step8(const AttnB& c, GWave8& w, int j) {
-  fetch_fp8<(SJ + 3) & 1>(c, w, j + 3);
+  fetch_fp8<(SJ + 3) & 1, PAGED>(c, w, j + 3);
   __builtin_amdgcn_sched_barrier(0);  // the loads go out before the widening
   store_fp8<(SJ + 2) % kStagesB, SJ & 1>(c, w);
   if (j < c.n_tiles) lds_barrier();
@@ -866,30 +891,47 @@ __device__ __forceinline__ void g_step8(const AttnB& c, GWave8& w, int j) {
 // j-1) and loads tile j+5's; with FP8 KV it also puts tile j+3's row scales
 // (loaded one step earlier) into the scale ring and loads tile j+4's. Then
 // score tile j+1 (stage (SJ+1)%4). The gather waves read tile j+4's slot in
-// step j+1, after this step's barrier.
-template <int SJ, bool FP8>
+// step j+1, after this step's barrier. Paged: tile j+4's pool rows come from
+// its positions (loaded two steps earlier) and blocks (loaded one step
+// earlier); this step loads tile j+5's blocks and tile j+6's positions.
+template <int SJ, bool FP8, bool PAGED>
 __device__ __forceinline__ void s_step(const AttnB& c, SWave& w, int j) {
   if (c.wave == 0) {
-    ring_put(c, j + 4, w.pn);
-    if (FP8) {
-      scale_put(c, j + 3, w.sn);
-      w.sn = load_scale(c, w.pn);
+    if (PAGED) {
+      const int32_t r4 = pool_row(c, w.pn, w.bn);
+      ring_put(c, j + 4, r4);
+      if (FP8) {
+        scale_put(c, j + 3, w.sn);
+        w.sn = load_scale(c, r4);
+      }
+      w.bn = load_blk(c, w.pn2);
+      w.pn = w.pn2;
+      w.pn2 = load_pos(c, j + 6);
+    } else {
+      ring_put(c, j + 4, w.pn);
+      if (FP8) {
+        scale_put(c, j + 3, w.sn);
+        w.sn = load_scale(c, w.pn);
+      }
+      w.pn = load_pos(c, j + 5);
     }
-    w.pn = load_pos(c, j + 5);
   }
-  if (j + 1 < c.n_tiles) s_phase<(SJ + 1) % kStagesB, FP8>(c, w, j + 1, (j + 1) & 1);
+  if (j + 1 < c.n_tiles) s_phase<(SJ + 1) % kStagesB, FP8, PAGED>(c, w, j + 1, (j + 1) & 1);
   lds_barrier();
 }
 
 // (kv without __restrict__: the FP8 gathers load it into registers, and a
 // restrict-qualified load may be moved across the barriers' memory clobbers,
 // away from the step that is meant to issue it)
-template <bool FP8>
+// Paged KV (PAGED): kv and kv_scale are pools of blocks of 2^lbs rows,
+// block_table [B][max_blocks] maps sequence blocks to pool blocks.
+template <bool FP8, bool PAGED>
 __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
     const uint16_t* __restrict__ q, const void* kv, const float* __restrict__ kv_scale,
     const int32_t* __restrict__ idx, int T, int L, int k, int rows_per_split, float sm_scale,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    float* __restrict__ part_lse, const int32_t* __restrict__ block_table, int max_blocks,
+    int lbs, int n_blocks) {
   __shared__ __attribute__((aligned(16))) uint8_t s_st0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_st1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_st2[kTileBytes];
@@ -917,7 +959,10 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   c.flag = s_flag;
   c.ring = s_ring;
   c.sring = s_sring;
-  c.kscale = FP8 ? kv_scale + (int64_t)b * L : nullptr;
+  c.kscale = FP8 ? (PAGED ? kv_scale : kv_scale + (int64_t)b * L) : nullptr;
+  c.btab = PAGED ? block_table + (int64_t)b * max_blocks : nullptr;
+  c.lbs = lbs;
+  c.nblk = n_blocks;
   c.lane = tid & 63;
   c.wave = tid >> 6;
   const Role role = role_of(c.wave);
@@ -949,6 +994,16 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
       p1 = load_pos(c, 1);
       p2 = load_pos(c, 2);
       w.pn = load_pos(c, 3);
+      if (PAGED) {
+        // pool rows of tiles 0..2; tile 3's blocks and tile 4's positions
+        // for step -1
+        w.pn2 = load_pos(c, 4);
+        const int32_t b0 = load_blk(c, p0), b1 = load_blk(c, p1), b2 = load_blk(c, p2);
+        w.bn = load_blk(c, w.pn);
+        p0 = pool_row(c, p0, b0);
+        p1 = pool_row(c, p1, b1);
+        p2 = pool_row(c, p2, b2);
+      }
       ring_put(c, 0, p0);
       ring_put(c, 1, p1);
       ring_put(c, 2, p2);
@@ -964,12 +1019,12 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
       scale_put(c, 1, s1);
     }
     lds_barrier();  // prologue (tile 0 landed)
-    s_step<3, FP8>(c, w, -1);  // scores tile 0 from stage 0
+    s_step<3, FP8, PAGED>(c, w, -1);  // scores tile 0 from stage 0
     for (int j = 0; j < c.n_tiles; j += kStagesB) {
-      s_step<0, FP8>(c, w, j);
-      if (j + 1 < c.n_tiles) s_step<1, FP8>(c, w, j + 1);
-      if (j + 2 < c.n_tiles) s_step<2, FP8>(c, w, j + 2);
-      if (j + 3 < c.n_tiles) s_step<3, FP8>(c, w, j + 3);
+      s_step<0, FP8, PAGED>(c, w, j);
+      if (j + 1 < c.n_tiles) s_step<1, FP8, PAGED>(c, w, j + 1);
+      if (j + 2 < c.n_tiles) s_step<2, FP8, PAGED>(c, w, j + 2);
+      if (j + 3 < c.n_tiles) s_step<3, FP8, PAGED>(c, w, j + 3);
     }
     // publish each head's exponent offset and sum
     float l_tot = w.l_run;
@@ -984,7 +1039,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   if (FP8 && role == kRoleGather) {
     GWave8 w;
     w.g = __builtin_amdgcn_readfirstlane(c.wave - 4);
-    w.kvb = (const uint8_t*)kv + (int64_t)b * L * kKvDim;
+    w.kvb = (const uint8_t*)kv + (PAGED ? 0 : (int64_t)b * L * kKvDim);
 #pragma unroll
     for (int i = 0; i < kFp8Per; ++i) {
       const int gi = 64 * (w.g + kGatherWaves * i) + c.lane;  // FP8 granule of the tile
@@ -996,17 +1051,17 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
     }
     __syncthreads();
     // prologue: tiles 0 and 1 loaded, tile 0 widened into stage 0
-    fetch_fp8<0>(c, w, 0);
-    fetch_fp8<1>(c, w, 1);
+    fetch_fp8<0, PAGED>(c, w, 0);
+    fetch_fp8<1, PAGED>(c, w, 1);
     __builtin_amdgcn_sched_barrier(0);
     store_fp8<0, 0>(c, w);
     lds_barrier();
-    g_step8<3>(c, w, -1);  // loads tile 2, widens tile 1 into stage 1
+    g_step8<3, PAGED>(c, w, -1);  // loads tile 2, widens tile 1 into stage 1
     for (int j = 0; j < c.n_tiles; j += kStagesB) {
-      g_step8<0>(c, w, j);
-      g_step8<1>(c, w, j + 1);
-      g_step8<2>(c, w, j + 2);
-      g_step8<3>(c, w, j + 3);
+      g_step8<0, PAGED>(c, w, j);
+      g_step8<1, PAGED>(c, w, j + 1);
+      g_step8<2, PAGED>(c, w, j + 2);
+      g_step8<3, PAGED>(c, w, j + 3);
     }
     wait_vm<0>();  // loads past the split's end are still in flight
     __syncthreads();
@@ -1015,7 +1070,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   if (!FP8 && role == kRoleGather) {
     GWave w;
     w.g = __builtin_amdgcn_readfirstlane(c.wave - 4);
-    w.kvb = (const uint8_t*)kv + (int64_t)b * L * kRowBytes;
+    w.kvb = (const uint8_t*)kv + (PAGED ? 0 : (int64_t)b * L * kRowBytes);
 #pragma unroll
     for (int i = 0; i < kDmaPerB; ++i) {
       const int o = 1024 * (w.g + kGatherWaves * i) + 16 * c.lane;  // LDS byte in the stage
@@ -1026,20 +1081,20 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
     }
     __syncthreads();
     // prologue: tiles 0 and 1 in flight, wait for tile 0
-    issue_tile_b<0>(c, w, 0);
+    issue_tile_b<0, PAGED>(c, w, 0);
     if (c.n_tiles > 1) {
-      issue_tile_b<1>(c, w, 1);
+      issue_tile_b<1, PAGED>(c, w, 1);
       wait_vm<kDmaPerB>();
     } else {
       wait_vm<0>();
     }
     lds_barrier();
-    g_step<3>(c, w, -1);  // issues tile 2 into stage 2, waits for tile 1
+    g_step<3, PAGED>(c, w, -1);  // issues tile 2 into stage 2, waits for tile 1
     for (int j = 0; j < c.n_tiles; j += kStagesB) {
-      g_step<0>(c, w, j);
-      if (j + 1 < c.n_tiles) g_step<1>(c, w, j + 1);
-      if (j + 2 < c.n_tiles) g_step<2>(c, w, j + 2);
-      if (j + 3 < c.n_tiles) g_step<3>(c, w, j + 3);
+      g_step<0, PAGED>(c, w, j);
+      if (j + 1 < c.n_tiles) g_step<1, PAGED>(c, w, j + 1);
+      if (j + 2 < c.n_tiles) g_step<2, PAGED>(c, w, j + 2);
+      if (j + 3 < c.n_tiles) g_step<3, PAGED>(c, w, j + 3);
     }
     __syncthreads();
     return;
@@ -1230,13 +1285,15 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
   }
   dim3 grid((unsigned)p.splits, (unsigned)queries);
   hipError_t e;
+  const int32_t* no_tab = nullptr;
   if (role_kernel && kv_fp8)
-    e = launch_kernel(sparse_mla_b_kernel<true>, grid, dim3(kThreadsB), 0, stream, q, kv, kv_scale,
-                      idx, T, L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
+    e = launch_kernel(sparse_mla_b_kernel<true, false>, grid, dim3(kThreadsB), 0, stream, q, kv,
+                      kv_scale, idx, T, L, k, p.rows_per_split, sm_scale, out, lse, part_o,
+                      part_lse, no_tab, 0, 0, 0);
   else if (role_kernel)
-    e = launch_kernel(sparse_mla_b_kernel<false>, grid, dim3(kThreadsB), 0, stream, q, kv,
+    e = launch_kernel(sparse_mla_b_kernel<false, false>, grid, dim3(kThreadsB), 0, stream, q, kv,
                       (const float*)nullptr, idx, T, L, k, p.rows_per_split, sm_scale, out, lse,
-                      part_o, part_lse);
+                      part_o, part_lse, no_tab, 0, 0, 0);
   else if (kv_fp8)
     e = launch_kernel(sparse_mla_kernel<true>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx, T,
                       L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
@@ -1244,6 +1301,40 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
     e = launch_kernel(sparse_mla_kernel<false>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx,
                       T, L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
   if (e != hipSuccess || p.splits <= 1) return e;
+  return launch_split_combine(part_o, part_lse, p.splits, queries, out, lse, stream);
+}
+
+hipError_t launch_sparse_mla_paged(const uint16_t* q, const void* kv, bool kv_fp8,
+                                   const float* kv_scale, const int32_t* block_table,
+                                   int max_blocks, int lbs, int n_blocks, const int32_t* idx,
+                                   int B, int T, int L, int k, float sm_scale, uint16_t* out,
+                                   float* lse, void* workspace, hipStream_t stream) {
+  // the split-role kernel with pool rows (64-bit gather offsets: no size limit)
+  const int64_t queries = (int64_t)B * T;
+  const SplitPlan p = plan_splits_b(queries, k);
+  uint16_t* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (p.splits > 1) {
+    part_o = (uint16_t*)workspace;
+    part_lse = (float*)(part_o + (size_t)queries * p.splits * kAttHeads * kLatent);
+  }
+  dim3 grid((unsigned)p.splits, (unsigned)queries);
+  hipError_t e;
+  if (kv_fp8)
+    e = launch_kernel(sparse_mla_b_kernel<true, true>, grid, dim3(kThreadsB), 0, stream, q, kv,
+                      kv_scale, idx, T, L, k, p.rows_per_split, sm_scale, out, lse, part_o,
+                      part_lse, block_table, max_blocks, lbs, n_blocks);
+  else
+    e = launch_kernel(sparse_mla_b_kernel<false, true>, grid, dim3(kThreadsB), 0, stream, q, kv,
+                      (const float*)nullptr, idx, T, L, k, p.rows_per_split, sm_scale, out, lse,
+                      part_o, part_lse, block_table, max_blocks, lbs, n_blocks);
+  if (e != hipSuccess || p.splits <= 1) return e;
+  return launch_split_combine(part_o, part_lse, p.splits, queries, out, lse, stream);
+}
+
+hipError_t launch_split_combine(const uint16_t* part_o, const float* part_lse, int splits,
+                                int64_t queries, uint16_t* out, float* lse, hipStream_t stream) {
+  const SplitPlan p{splits, 0};
   const int64_t per = (int64_t)kAttHeads * kLatent;
   if (p.splits <= kCombBatch)
     return launch_kernel(combine_kernel<1>, dim3(32, (unsigned)queries), dim3(256), 0, stream,

@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_function():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -135,6 +135,33 @@ def test_context_parallel_validation():
     assert comb(P, P, 1025, 1, 1, P, None, None) == SHAPE
     assert comb(P, P, 2, 1, 1, None, None, None) == NULL
     assert comb(P, P, 2, 1, 1, P, P + 4, None) == SHAPE
+
+
+class _Pg(ctypes.Structure):
+    _fields_ = [("block_table", _v), ("max_blocks", _i), ("block_size", _i), ("n_blocks", _i)]
+
+
+def test_paged_validation():
+    idx_p = _fn("lcs_idx_score_paged", [_v] * 7 + [_i] * 3 + [_v, _v])
+    attn_p = _fn("lcs_sparse_mla_attn_paged", [_v, _v, ctypes.c_int, _v, _v, _v] + [_i] * 4
+                 + [_f, _v, _v, _v, _z, _v])
+    app_p = _fn("lcs_cache_append_paged", [_v, _v, ctypes.c_int, _v] + [_i] * 3 + [_v] * 6)
+
+    def pg(bt=P, mb=16, bs=64, nb=100):
+        return ctypes.byref(_Pg(bt, mb, bs, nb))
+    assert idx_p(P, P, P, P, P, None, P, 1, 1, 1000, P, None) == NULL and b"paged" in last()
+    assert idx_p(P, P, P, P, P, pg(bt=None), P, 1, 1, 1000, P, None) == NULL
+    assert idx_p(P, P, P, P, P, pg(bs=32), P, 1, 1, 1000, P, None) == UNSUP
+    assert idx_p(P, P, P, P, P, pg(bs=96), P, 1, 1, 1000, P, None) == UNSUP
+    assert idx_p(P, P, P, P, P, pg(mb=15), P, 1, 1, 1000, P, None) == SHAPE  # 15 * 64 < 1000
+    assert idx_p(P, P, P, P, P, pg(nb=1 << 26), P, 1, 1, 1000, P, None) == SHAPE  # 2^32 rows
+    assert idx_p(P, P, P, P, P, pg(nb=0), P, 1, 1, 1000, P, None) == SHAPE
+    need = lcs.attn_workspace_bytes(2, 1, 2048)
+    assert attn_p(P, P, 1, None, pg(), P, 2, 1, 1000, 2048, 1 / 24, P, None, P, need, None) == NULL
+    assert attn_p(P, P, 0, None, pg(bs=100), P, 2, 1, 1000, 2048, 1 / 24, P, None, P, need,
+                  None) == UNSUP
+    assert app_p(None, P, 0, P, 1, 1, 1000, pg(mb=1), None, None, P, None, None) == SHAPE
+    assert app_p(None, P, 0, P, 1, 1, 1000, None, None, None, P, None, None) == NULL
 
 
 def test_schedules_and_counts():
