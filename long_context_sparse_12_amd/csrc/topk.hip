@@ -107,9 +107,36 @@ __device__ __forceinline__ uint32_t block_prefix_small(uint32_t c, uint32_t* s_w
   return before + wp;
 }
 
+// Block-wide exclusive prefix of one uint32 per thread: an inclusive scan
+// inside each wave (shuffles), then the wave totals through LDS (s_tmp holds
+// kWavesTk entries). Returns the exclusive prefix; total in `tot`.
+__device__ uint32_t block_prefix(uint32_t v, uint32_t* s_tmp, uint32_t& tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t up = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += up;
+  }
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWavesTk; ++i) {
+    const uint32_t t = s_tmp[i];
+    before += i < wave ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  return before + incl - v;
+}
+
 // Find bucket b of hist[nb] (LDS) with  above(b) < need <= above(b) + hist[b],
 // where above(b) = sum of hist over buckets > b. Result in s_out[0] (bucket)
-// and s_out[1] (above). Requires sum(hist) >= need >= 1.
+// and s_out[1] (above). Requires sum(hist) >= need >= 1. Thread t sums buckets
+// [t BPT, (t + 1) BPT); a block prefix of those sums (shuffles in each wave,
+// the wave totals through LDS) gives every thread the count above its range.
 template <int NB>
 __device__ void select_bucket(const uint32_t* hist, uint32_t need, uint32_t* s_scan,
                               uint32_t* s_out) {
@@ -121,20 +148,9 @@ __device__ void select_bucket(const uint32_t* hist, uint32_t need, uint32_t* s_s
 #pragma unroll
     for (int i = 0; i < BPT; ++i) local += hist[tid * BPT + i];
   }
-  // suffix sums over threads: s_scan[t] = sum of local over threads > t
-  s_scan[tid] = local;
-  __syncthreads();
-  if (tid < kWavesTk) {
-    // per-wave totals into slots kThreads + wave
-    uint32_t s = 0;
-    for (int i = 0; i < 64; ++i) s += s_scan[tid * 64 + i];
-    s_scan[kThreads + tid] = s;
-  }
-  __syncthreads();
-  const int wave = tid >> 6, lane = tid & 63;
-  uint32_t above = 0;
-  for (int wv = wave + 1; wv < kWavesTk; ++wv) above += s_scan[kThreads + wv];
-  for (int i = lane + 1; i < 64; ++i) above += s_scan[wave * 64 + i];
+  uint32_t tot;
+  const uint32_t before = block_prefix(local, s_scan, tot);
+  const uint32_t above = tot - before - local;
   if (tid < ACTIVE && above < need && need <= above + local) {
     uint32_t run = above;
     for (int i = BPT - 1; i >= 0; --i) {
@@ -165,7 +181,20 @@ __global__ void __launch_bounds__(kThreads) topk_hist_kernel(
   for (int i = tid; i < kBins1; i += kThreads) hist[i] = 0;
   __syncthreads();
   const float* srow = scores + (size_t)row * L;
-  for (int s = begin + tid; s < end; s += kThreads) atomicAdd(&hist[score_key(srow[s]) >> 20], 1u);
+  // kHistPer loads of a thread in flight together, then their atomics (a
+  // load per iteration would wait one memory latency per element)
+  constexpr int kHistPer = kMinChunk * 2 / kThreads;  // 8
+  for (int base = begin; base < end; base += kThreads * kHistPer) {
+    float v[kHistPer];
+#pragma unroll
+    for (int j = 0; j < kHistPer; ++j) {
+      const int s = base + kThreads * j + tid;
+      v[j] = s < end ? srow[s] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kHistPer; ++j)
+      if (base + kThreads * j + tid < end) atomicAdd(&hist[score_key(v[j]) >> 20], 1u);
+  }
   __syncthreads();
   for (int i = tid; i < kBins1; i += kThreads) {
     const uint32_t c = hist[i];
@@ -211,7 +240,22 @@ __global__ void __launch_bounds__(kThreads) topk_filter_kernel(
   uint32_t* my = lists + ((size_t)row * chunks + blockIdx.x) * (size_t)chunk;
   uint32_t written = 0;
   int parity = 0;
+  // the next block's four scores per thread are loaded before this block's
+  // scan barrier, so that their latency overlaps it
+  float nv[4];
+  auto load4 = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = base + 4 * tid + j;
+      nv[j] = s < end ? srow[s] : 0.f;
+    }
+  };
+  load4(begin);
   for (int base = begin; base < end; base += 4 * kThreads) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = nv[j];
+    if (base + 4 * kThreads < end) load4(base + 4 * kThreads);
     uint32_t e[4];
     uint32_t c = 0;
 #pragma unroll
@@ -219,7 +263,7 @@ __global__ void __launch_bounds__(kThreads) topk_filter_kernel(
       const int s = base + 4 * tid + j;
       e[j] = 0;
       if (s < end) {
-        const uint32_t d = score_key(srow[s]) >> 20;
+        const uint32_t d = score_key(v[j]) >> 20;
         if (d >= b1) {
           e[j] = (uint32_t)s | (d > b1 ? kSure : 0u) | 0x40000000u;  // bit 30: valid
           ++c;
@@ -237,30 +281,7 @@ __global__ void __launch_bounds__(kThreads) topk_filter_kernel(
   if (tid == 0) counts[(size_t)row * chunks + blockIdx.x] = written;
 }
 
-// Block-wide exclusive prefix of one uint32 per thread: an inclusive scan
-// inside each wave (shuffles), then the wave totals through LDS (s_tmp holds
-// kWavesTk entries). Returns the exclusive prefix; total in `tot`.
-__device__ uint32_t block_prefix(uint32_t v, uint32_t* s_tmp, uint32_t& tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t up = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += up;
-  }
-  if (lane == 63) s_tmp[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0;
-  tot = 0;
-#pragma unroll
-  for (int i = 0; i < kWavesTk; ++i) {
-    const uint32_t t = s_tmp[i];
-    before += i < wave ? t : 0u;
-    tot += t;
-  }
-  __syncthreads();
-  return before + incl - v;
-}
+
 
 // Candidates a row can stage in LDS for the fast path of the final kernel
 constexpr int kStage = 16384;
