@@ -453,6 +453,189 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// One workgroup per row, for rows of at most kRowMaxL positions: the four
+// launches above in one, with the candidate lists in LDS. Histogram of the top
+// 12 key bits (coalesced loads, a thread's 8 in flight before its atomics),
+// the threshold bucket b1, then every wave compacts its own contiguous eighth
+// of the row in position order (a ballot per 64 positions) into its LDS list
+// (kRowCap entries: position | sure flag, and the key); entries past kRowCap
+// go to the wave's slice of `spill` (positions only; their keys are re-read
+// from the scores). Two more digits (12 + 8 bits) over the candidates fix the
+// threshold key tau and how many keys equal to tau are kept, and the lists are
+// emitted in wave order (= position order): the keys above tau and the first
+// ties. Each row's scores are read twice, from one CU: a single workgroup
+// keeps at most ~64 KB of loads in flight, so the row kernel pays only where
+// many rows fill the chip (chunked prefill); a few long rows (decode) use the
+// chunked launches, which spread each row over many CUs.
+constexpr int kRowMaxL = 1 << 18;
+constexpr int kRowMinRows = 512;
+constexpr int kRowCap = 2048;  // LDS list entries per wave (8 waves: 16384)
+
+__global__ void __launch_bounds__(kThreads) topk_row_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ vis_len, int L, int k,
+    int spill_stride, uint32_t* __restrict__ spill, int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[kBins1];
+  __shared__ uint32_t s_ent[kWavesTk][kRowCap];
+  __shared__ uint32_t s_key[kWavesTk][kRowCap];
+  __shared__ uint32_t s_scan[kThreads + kWavesTk];
+  __shared__ uint32_t s_out[2];
+  __shared__ uint32_t s_cnt[kWavesTk], s_tie[kWavesTk], s_sel[kWavesTk];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int vis = clamp_vis(vis_len[row], L);
+  int32_t* out = idx + (size_t)row * k;
+  if (vis <= k) {
+    // every visible position is kept: positions in order, then -1 padding
+    for (int i = tid; i < k; i += kThreads) out[i] = i < vis ? i : -1;
+    return;
+  }
+  const float* srow = scores + (size_t)row * L;
+
+  // ---- pass 1: histogram of key bits 31..20 ----
+  for (int i = tid; i < kBins1; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  constexpr int kPer = 32;  // loads of a thread in flight before its atomics
+  for (int base = 0; base < vis; base += kThreads * kPer) {
+    float v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int p = base + kThreads * j + tid;
+      v[j] = p < vis ? srow[p] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (base + kThreads * j + tid < vis) atomicAdd(&hist[score_key(v[j]) >> 20], 1u);
+  }
+  __syncthreads();
+  select_bucket<kBins1>(hist, (uint32_t)k, s_scan, s_out);
+  const uint32_t b1 = s_out[0];
+  const uint32_t n_above = s_out[1];
+
+  // ---- pass 2: ordered compaction, wave w over positions [w seg, (w+1) seg) ----
+  const int seg = (vis + kWavesTk - 1) / kWavesTk;
+  const int seg_cap = spill_stride / kWavesTk;  // >= seg: spill_stride >= L, a multiple of 8
+  const int p0 = wave * seg, p1 = min(vis, p0 + seg);
+  uint32_t* my_spill = spill + (size_t)row * spill_stride + (size_t)wave * seg_cap;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t cnt = 0;
+  constexpr int kPer2 = 16;  // loads of a lane in flight per step
+  for (int base = p0; base < p1; base += kPer2 * 64) {
+    float v[kPer2];
+#pragma unroll
+    for (int j = 0; j < kPer2; ++j) {
+      const int p = base + 64 * j + lane;
+      v[j] = p < p1 ? srow[p] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer2; ++j) {
+      const int p = base + 64 * j + lane;
+      const uint32_t key = score_key(v[j]);
+      const bool q = p < p1 && (key >> 20) >= b1;
+      const uint64_t m = __ballot(q);
+      if (q) {
+        const uint32_t slot = cnt + (uint32_t)__popcll(m & lt);
+        const uint32_t e = (uint32_t)p | ((key >> 20) > b1 ? kSure : 0u);
+        if (slot < (uint32_t)kRowCap) {
+          s_ent[wave][slot] = e;
+          s_key[wave][slot] = key;
+        } else {
+          my_spill[slot] = e;
+        }
+      }
+      cnt += (uint32_t)__popcll(m);
+    }
+  }
+  if (lane == 0) s_cnt[wave] = cnt;
+  __syncthreads();
+
+  // entry e of wave w's list and its key (keys of spilled candidates re-read)
+  auto get = [&](int w, uint32_t e, uint32_t& key) -> uint32_t {
+    if (e < (uint32_t)kRowCap) {
+      key = s_key[w][e];
+      return s_ent[w][e];
+    }
+    const uint32_t v = spill[(size_t)row * spill_stride + (size_t)w * seg_cap + e];
+    key = (v & kSure) ? 0u : score_key(srow[v & ~kSure]);
+    return v;
+  };
+  const uint32_t my_n = s_cnt[wave];
+
+  // ---- digit 2 (bits 19..8), then digit 3 (bits 7..0), over the candidates ----
+  const uint32_t need1 = (uint32_t)k - n_above;
+  for (int i = tid; i < kBins2; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  for (uint32_t e = lane; e < my_n; e += 64) {
+    uint32_t key;
+    const uint32_t v = get(wave, e, key);
+    if (!(v & kSure)) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
+  }
+  __syncthreads();
+  select_bucket<kBins2>(hist, need1, s_scan, s_out);
+  const uint32_t b2 = s_out[0];
+  const uint32_t above2 = s_out[1];
+  __syncthreads();
+  for (int i = tid; i < kBins3; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  const uint32_t pre12 = (b1 << 12) | b2;
+  for (uint32_t e = lane; e < my_n; e += 64) {
+    uint32_t key;
+    const uint32_t v = get(wave, e, key);
+    if (!(v & kSure) && (key >> 8) == pre12) atomicAdd(&hist[key & 0xFFu], 1u);
+  }
+  __syncthreads();
+  const uint32_t need2 = need1 - above2;
+  select_bucket<kBins3>(hist, need2, s_scan, s_out);
+  const uint32_t tau = (pre12 << 8) | s_out[0];
+  const uint32_t need_tie = need2 - s_out[1];  // keys equal to tau that are kept
+
+  // ---- emission in position order (wave order, then list order) ----
+  // ties per wave, then each wave's kept count, then the writes
+  uint32_t my_ties = 0;
+  for (uint32_t e0 = 0; e0 < my_n; e0 += 64) {
+    const uint32_t e = e0 + lane;
+    uint32_t key = 0, v = kSure;
+    if (e < my_n) v = get(wave, e, key);
+    my_ties += (uint32_t)__popcll(__ballot(e < my_n && !(v & kSure) && key == tau));
+  }
+  if (lane == 0) s_tie[wave] = my_ties;
+  __syncthreads();
+  uint32_t ties_before = 0;
+  for (int w = 0; w < wave; ++w) ties_before += s_tie[w];
+  auto walk = [&](bool write, uint32_t out_base) -> uint32_t {
+    uint32_t tie_rank = ties_before, kept = 0;
+    for (uint32_t e0 = 0; e0 < my_n; e0 += 64) {
+      const uint32_t e = e0 + lane;
+      uint32_t key = 0, v = 0;
+      bool in = e < my_n;
+      if (in) v = get(wave, e, key);
+      const bool sure = in && (v & kSure);
+      const bool tie = in && !sure && key == tau;
+      const uint64_t tm = __ballot(tie);
+      const uint32_t my_rank = tie_rank + (uint32_t)__popcll(tm & lt);
+      const bool sel = sure || (in && !sure && key > tau) || (tie && my_rank < need_tie);
+      const uint64_t sm = __ballot(sel);
+      if (write && sel) {
+        const uint32_t at = out_base + kept + (uint32_t)__popcll(sm & lt);
+        if (at < (uint32_t)k) out[at] = (int32_t)(v & ~kSure);
+      }
+      tie_rank += (uint32_t)__popcll(tm);
+      kept += (uint32_t)__popcll(sm);
+    }
+    return kept;
+  };
+  const uint32_t my_kept = walk(false, 0);
+  if (lane == 0) s_sel[wave] = my_kept;
+  __syncthreads();
+  uint32_t kept_before = 0, kept_total = 0;
+  for (int w = 0; w < kWavesTk; ++w) {
+    kept_before += w < wave ? s_sel[w] : 0u;
+    kept_total += s_sel[w];
+  }
+  walk(true, kept_before);
+  for (int i = (int)kept_total + tid; i < k; i += kThreads) out[i] = -1;
+}
+
 // zero the row histograms (rows that span several chunks accumulate into them)
 __global__ void __launch_bounds__(256) topk_clear_kernel(uint32_t* __restrict__ ghist) {
   uint4* h = (uint4*)(ghist + (size_t)blockIdx.x * kBins1);
@@ -473,6 +656,9 @@ hipError_t launch_topk(const float* scores, const int32_t* vis_len, int rows, in
   uint32_t* ghist = (uint32_t*)(ws + ly.off_hist);
   uint32_t* counts = (uint32_t*)(ws + ly.off_counts);
   uint32_t* lists = (uint32_t*)(ws + ly.off_lists);
+  if (L <= kRowMaxL && rows >= kRowMinRows)  // one workgroup per row; spills in the list area
+    return launch_kernel(topk_row_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores,
+                         vis_len, L, k, ly.chunks * ly.chunk, lists, idx);
   dim3 grid((unsigned)ly.chunks, (unsigned)rows);
   hipError_t e = hipSuccess;
   if (ly.chunks > 1) {

@@ -128,6 +128,9 @@ TOPK_CASES = [
     ("normal", 1, 2, 131072, 2048), ("planted", 2, 1, 131072, 2048), ("normal", 1, 300, 4001, 2048),
     ("ragged", 1, 5, 3001, 2048), ("normal", 1, 1, 1 << 20, 2048), ("ties", 1, 1, 1 << 20, 2048),
     ("normal", 2, 2, 1, 1), ("normal", 1, 1, 2048, 2048),
+    # >= 512 rows of <= 2^18 positions: the one-workgroup-per-row kernel
+    ("normal", 1, 600, 4001, 2048), ("ragged", 1, 520, 20000, 2048),
+    ("signed-zero", 2, 256, 3000, 1000), ("ties", 4, 128, 9000, 2048),
 ]
 
 
@@ -149,6 +152,30 @@ def test_topk_bit_exact_on_oracle_scores(case):
     idx2 = torch.full((B, T, k), -9, dtype=torch.int32, device=DEV)
     lcs.topk_select(ds, dv, k, idx2, ws)
     assert torch.equal(idx, idx2)
+
+
+@pytest.mark.parametrize("name", ["equal", "ties7"])
+def test_topk_row_kernel_spills(name):
+    """512 identical rows of 2^18 positions (the row kernel's largest L): with
+    all-equal or 7-valued scores a wave's list gets up to 32768 entries, 2048
+    in LDS and the rest in the workspace. Every row must give the oracle's
+    selection of that row."""
+    _say("case: topk row kernel spill %s" % name)
+    B, T, L, k = 1, 512, 1 << 18, 2048
+    rs = np.random.default_rng(7)
+    if name == "equal":
+        row = np.full(L, -1.5, np.float32)
+    else:
+        row = rs.choice(np.array([-3.0, -1.0, 0.0, 0.5, 2.0, 4.0, 9.0], np.float32), size=L)
+    ref = oracle.topk(row[None, None, :], np.array([[L]], np.int32), k)[0, 0]
+    ds = torch.from_numpy(row).to(DEV).view(1, 1, L).expand(B, T, L).contiguous()
+    dv = torch.full((B, T), L, dtype=torch.int32, device=DEV)
+    idx = torch.full((B, T, k), -7, dtype=torch.int32, device=DEV)
+    ws = _zeros(lcs.topk_workspace_bytes(B, T, L, k))
+    lcs.topk_select(ds, dv, k, idx, ws)
+    got = idx.cpu().numpy()[0]
+    bad = np.argwhere(np.any(got != ref[None, :], axis=-1))
+    assert bad.size == 0, "rows differ: %s" % bad[:5].tolist()
 
 
 def test_topk_workspace_reused_across_shapes():
