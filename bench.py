@@ -36,8 +36,8 @@ ROTATIONS = 3  # query sets cycled between steps so no step reuses another's gat
 # scaled by the copy-kernel calibration; valid only for the kernel source it was
 # taken on (sha256 of csrc/idx_score.hip, first 16 hex digits).
 TRAFFIC = {
-    "decode-B32-L131072-group4": {"sha": "bdd7ba82131a2a60", "bytes": 572063033},
-    "decode-B2-L1048576-78layers-fp8kv": {"sha": "bdd7ba82131a2a60", "bytes": 285347196},
+    "decode-B32-L131072-group4": {"sha": "0935792a44d60bbb", "bytes": 572064057},
+    "decode-B2-L1048576-78layers-fp8kv": {"sha": "0935792a44d60bbb", "bytes": 285362761},
 }
 
 

@@ -76,8 +76,9 @@ typedef enum { LCS_KV_BF16 = 0, LCS_KV_FP8_E4M3 = 1 } lcs_kv_dtype;
  * scores  [B][T][L]       fp32 output:
  *   scores[b,t,s] = k_scale[s] * sum_j w[j]*q_scale[j] * relu(q8[j] . k8[s])
  *   for s < vis_len[b,t], -inf otherwise.
- * T <= 4 uses a key-streaming kernel (one pass over the keys, the 32 heads
- * as the FP8 MFMA M dimension); larger T uses a tiled FP8 MFMA kernel. */
+ * T < 16 uses a key-streaming kernel (one pass over the keys per group of
+ * up to 6 queries, the 32 heads as the FP8 MFMA M dimension); T >= 16 uses a
+ * tiled FP8 MFMA kernel. */
 lcs_status lcs_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
                          const uint8_t* k8, const float* k_scale,
                          const int32_t* vis_len, int32_t B, int32_t T, int32_t L,

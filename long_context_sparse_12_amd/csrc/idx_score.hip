@@ -6,7 +6,8 @@
 // lightning-indexer form I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]) with FP8
 // queries and keys, each with a per-row dequantisation scale.
 //
-// Decode (T <= 4): every key is read once from HBM; each wave runs the 32
+// Decode (T < 16, up to 6 queries per pass over the keys): every key is read
+// once from HBM per pass; each wave runs the 32
 // heads of a query as the M dimension of v_mfma_f32_32x32x64_f8f6f4 against
 // 32 keys as N, then folds ReLU * (w * q_scale) over its heads and scales by
 // the key's scale. 132 bytes of HBM traffic per key, no reuse, so the kernel
@@ -78,6 +79,11 @@ __device__ __forceinline__ float sum_pair(float x, float y) {
 // 64-key tile starts at a multiple of 64, so it lies in one block; the
 // workgroup's slice of the table (at most 65 entries) sits in LDS.
 constexpr int kMaxWgBlocks = LCS_IDX_MAX_ITERS * kWaves * kSuper / 64 + 1;
+// Up to kMaxTq queries share each key tile, so a multi-token verify of up to
+// 6 tokens reads the keys once. Past 4 queries the combined head weights
+// (w * q_scale, 16 per lane and query) move from registers to LDS, which the
+// registers of the queries' MFMA operands would otherwise overrun.
+constexpr int kMaxTq = 6;
 template <int TQ, bool PAGED>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 1 ? 4 : 2))) idx_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
@@ -85,14 +91,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
     const float* __restrict__ k_scale, const int32_t* __restrict__ vis_len, int T,
     int t0, int L, int keys_per_wg, float* __restrict__ scores,
     const int32_t* __restrict__ block_table, int max_blocks, int lbs, int n_blocks) {
+  constexpr bool kWqLds = TQ > 4;
   __shared__ int32_t s_blk[PAGED ? kMaxWgBlocks : 1];
+  // [query][lane half][16]: the weights of the 16 heads a lane half holds
+  __shared__ __attribute__((aligned(16))) float s_wq[kWqLds ? TQ * 2 * 16 : 1];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int ln = lane & 31, hh = lane >> 5;
 
   v8i aq[TQ][2];
-  float wq[TQ][16];
+  float wq[kWqLds ? 1 : TQ][16];
   int vis[TQ];
 #pragma unroll
   for (int t = 0; t < TQ; ++t) {
@@ -100,12 +109,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
     const uint8_t* qrow = q8 + (bt * kIdxHeads + ln) * kIdxDim + 32 * hh;
     aq[t][0] = *(const v8i*)(qrow);
     aq[t][1] = *(const v8i*)(qrow + 64);
+    if (!kWqLds) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int hd = 8 * (i >> 2) + 4 * hh + (i & 3);
-      wq[t][i] = w[bt * kIdxHeads + hd] * q_scale[bt * kIdxHeads + hd];
+      for (int i = 0; i < 16; ++i) {
+        const int hd = 8 * (i >> 2) + 4 * hh + (i & 3);
+        wq[t][i] = w[bt * kIdxHeads + hd] * q_scale[bt * kIdxHeads + hd];
+      }
     }
     vis[t] = clamp_vis(vis_len[bt], L);
+  }
+  if (kWqLds) {
+    if ((int)threadIdx.x < TQ * 32) {
+      const int t = threadIdx.x >> 5, h2 = (threadIdx.x >> 4) & 1, i = threadIdx.x & 15;
+      const int hd = 8 * (i >> 2) + 4 * h2 + (i & 3);
+      const int64_t o = ((int64_t)b * T + t0 + t) * kIdxHeads + hd;
+      s_wq[(t * 2 + h2) * 16 + i] = w[o] * q_scale[o];
+    }
+    __syncthreads();
   }
 
   const int64_t key_base_b = (int64_t)b * L;
@@ -161,8 +181,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
         v16f d = mfma_fp8_32x32x64(aq[t][0], bv[2 * blk]);
         d = mfma_fp8_32x32x64_acc(aq[t][1], bv[2 * blk + 1], d);
         float p = 0.f;
+        if (kWqLds) {
+          const v4f* wl = (const v4f*)(s_wq + (t * 2 + hh) * 16);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) p = fmaf(wq[t][i], relu(d[i]), p);
+          for (int m = 0; m < 4; ++m) {
+            const v4f wv = wl[m];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p = fmaf(wv[e], relu(d[4 * m + e]), p);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) p = fmaf(wq[kWqLds ? 0 : t][i], relu(d[i]), p);
+        }
         r[blk] = sum_halves(p);
       }
       const float res = hh ? r[1] : r[0];  // lane l holds key tile_base + l
@@ -170,6 +200,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
         const int64_t bt = (int64_t)b * T + t0 + t;
         scores[bt * L + my_key] = my_key < vis[t] ? res * ks : -INFINITY;
       }
+      // past 4 queries, one query's MFMA results at a time (the scheduler
+      // would otherwise hold every query's in registers at once)
+      if (kWqLds) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -429,31 +462,27 @@ hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float*
   if (iters > LCS_IDX_MAX_ITERS) iters = LCS_IDX_MAX_ITERS;
   const int kpw = (int)(iters * kWaves * kSuper);
   dim3 grid((unsigned)((L + kpw - 1) / kpw), (unsigned)B);
-  for (int t0 = 0; t0 < T; t0 += 4) {
-    const int tq = T - t0 < 4 ? T - t0 : 4;
+  for (int t0 = 0; t0 < T; t0 += kMaxTq) {
+    const int tq = T - t0 < kMaxTq ? T - t0 : kMaxTq;
     hipError_t e;
+#define LCS_DECODE_CASE(N)                                                                      \
+  case N:                                                                                       \
+    e = launch_kernel(idx_decode_kernel<N, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w, k8, \
+                      k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs, n_blocks);   \
+    break;
     switch (tq) {
-      case 1:
-        e = launch_kernel(idx_decode_kernel<1, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w,
-                          k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
-                          n_blocks);
-        break;
-      case 2:
-        e = launch_kernel(idx_decode_kernel<2, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w,
-                          k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
-                          n_blocks);
-        break;
-      case 3:
-        e = launch_kernel(idx_decode_kernel<3, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w,
-                          k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
-                          n_blocks);
-        break;
+      LCS_DECODE_CASE(1)
+      LCS_DECODE_CASE(2)
+      LCS_DECODE_CASE(3)
+      LCS_DECODE_CASE(4)
+      LCS_DECODE_CASE(5)
       default:
-        e = launch_kernel(idx_decode_kernel<4, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w,
-                          k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
+        e = launch_kernel(idx_decode_kernel<kMaxTq, PAGED>, grid, dim3(256), 0, stream, q8, q_scale,
+                          w, k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
                           n_blocks);
         break;
     }
+#undef LCS_DECODE_CASE
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -49,9 +49,10 @@ def test_device_generator_matches_host():
 
 
 # ------------------------------------------------------------------ indexer
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 16, 24, 37])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8, 16, 24, 37])
 def test_idx_score_matches_oracle(T):
-    """T < 16: the key-streaming kernel (T > 4 in chunks of 4); T >= 16: the
+    """T < 16: the key-streaming kernel (up to 6 queries per pass, T = 7 and 8
+    in two passes); T >= 16: the
     tiled prefill kernel (8-query chunks, 1024-key blocks; L = 8229 leaves a
     ragged last block and T = 37 a ragged last chunk)."""
     _say("case: idx_score T=%d" % T)
