@@ -451,6 +451,11 @@ lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers, lcs
   }
 
   const size_t per = (size_t)B * T * k;
+  // One query per sequence: the indexer also builds the selection's first
+  // histogram. The selection re-zeroes it, so one clear serves every full layer.
+  const bool fused_hist = T == 1 && lcs::topk_takes_prebuilt_hist((int64_t)B * T, L);
+  if (fused_hist)
+    TRY(hip_status(lcs::launch_topk_clear(ws_topk, B * T, L, stream), "topk clear launch"));
   int32_t* cur = nullptr;
   int32_t nfull = 0;
   for (int32_t l = 0; l < n_layers; ++l) {
@@ -459,11 +464,21 @@ lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers, lcs
     if (full) {
       cur = idx_out + (size_t)nfull * per;
       ++nfull;
-      TRY(hip_status(lcs::launch_idx_score(ly.q8, ly.q_scale, ly.w, ly.k8, ly.k_scale, vis_len, B,
-                                           T, L, scores_scratch, stream),
-                     "idx_score launch"));
-      TRY(hip_status(lcs::launch_topk(scores_scratch, vis_len, B * T, L, k, cur, ws_topk, stream),
-                     "topk launch"));
+      if (fused_hist) {
+        TRY(hip_status(lcs::launch_idx_score_hist(ly.q8, ly.q_scale, ly.w, ly.k8, ly.k_scale,
+                                                  vis_len, B, L, scores_scratch,
+                                                  lcs::topk_hist_area(ws_topk, B, L), stream),
+                       "idx_score launch"));
+        TRY(hip_status(lcs::launch_topk_prebuilt(scores_scratch, vis_len, B, L, k, cur, ws_topk,
+                                                 stream),
+                       "topk launch"));
+      } else {
+        TRY(hip_status(lcs::launch_idx_score(ly.q8, ly.q_scale, ly.w, ly.k8, ly.k_scale, vis_len,
+                                             B, T, L, scores_scratch, stream),
+                       "idx_score launch"));
+        TRY(hip_status(lcs::launch_topk(scores_scratch, vis_len, B * T, L, k, cur, ws_topk, stream),
+                       "topk launch"));
+      }
     }
     // KV Share: every MTP draft step reads the first step's cache
     const lcs_layer& kvl = mtp_steps > 0 ? layers[0] : ly;

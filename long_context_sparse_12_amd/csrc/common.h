@@ -102,6 +102,23 @@ size_t topk_workspace_bytes(int64_t rows, int L, int k);
 hipError_t launch_topk(const float* scores, const int32_t* vis_len, int rows, int L, int k,
                        int32_t* idx, void* workspace, hipStream_t stream);
 
+// Decode steps with one query per sequence can build the selection's first
+// radix-digit histogram inside the indexer launch: launch_topk_clear zeroes
+// the histograms in the top-k workspace (topk_hist_area), launch_idx_score_hist
+// scores and accumulates them, and launch_topk_prebuilt selects without a
+// histogram pass. Every chunked selection leaves the histograms zero again, so
+// the clear is needed once per workspace, before the first such indexer launch.
+// topk_takes_prebuilt_hist: the selection for these shapes uses the chunked
+// launches (the only ones that read the histograms).
+bool topk_takes_prebuilt_hist(int64_t rows, int L);
+uint32_t* topk_hist_area(void* workspace, int64_t rows, int L);
+hipError_t launch_topk_clear(void* workspace, int rows, int L, hipStream_t stream);
+hipError_t launch_topk_prebuilt(const float* scores, const int32_t* vis_len, int rows, int L,
+                                int k, int32_t* idx, void* workspace, hipStream_t stream);
+hipError_t launch_idx_score_hist(const uint8_t* q8, const float* q_scale, const float* w,
+                                 const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
+                                 int B, int L, float* scores, uint32_t* hist, hipStream_t stream);
+
 size_t attn_workspace_bytes(int64_t queries, int k);
 hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
                              const float* kv_scale, const int32_t* idx, int B, int T, int L,

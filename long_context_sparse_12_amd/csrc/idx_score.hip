@@ -84,21 +84,33 @@ constexpr int kMaxWgBlocks = LCS_IDX_MAX_ITERS * kWaves * kSuper / 64 + 1;
 // (w * q_scale, 16 per lane and query) move from registers to LDS, which the
 // registers of the queries' MFMA operands would otherwise overrun.
 constexpr int kMaxTq = 6;
-template <int TQ, bool PAGED>
+// HIST (one query per sequence, T = 1): the kernel also counts its visible
+// scores by their top 12 key bits (the first radix digit of the top-k
+// selection) in an LDS histogram and adds it into hist[b][4096] at the end,
+// so the selection needs no pass of its own over the scores to build it.
+constexpr int kHistBins = 4096;
+template <int TQ, bool PAGED, bool HIST = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 1 ? 4 : 2))) idx_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const int32_t* __restrict__ vis_len, int T,
     int t0, int L, int keys_per_wg, float* __restrict__ scores,
-    const int32_t* __restrict__ block_table, int max_blocks, int lbs, int n_blocks) {
+    const int32_t* __restrict__ block_table, int max_blocks, int lbs, int n_blocks,
+    uint32_t* __restrict__ hist) {
+  static_assert(!HIST || (TQ == 1 && !PAGED), "the fused histogram is built for T = 1 only");
   constexpr bool kWqLds = TQ > 4;
   __shared__ int32_t s_blk[PAGED ? kMaxWgBlocks : 1];
   // [query][lane half][16]: the weights of the 16 heads a lane half holds
   __shared__ __attribute__((aligned(16))) float s_wq[kWqLds ? TQ * 2 * 16 : 1];
+  __shared__ uint32_t s_hist[HIST ? kHistBins : 1];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int ln = lane & 31, hh = lane >> 5;
+  if (HIST) {
+    for (int i = threadIdx.x; i < kHistBins; i += 256) s_hist[i] = 0u;
+    __syncthreads();
+  }
 
   v8i aq[TQ][2];
   float wq[kWqLds ? 1 : TQ][16];
@@ -141,7 +153,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
   }
 
   int base = wg_begin + wave * kSuper;
-  if (base >= wg_end) return;
+  if (!HIST && base >= wg_end) return;
 
   // keys [tile_base + 32 blk + ln], K halves 0 and 1, and the scale of key
   // tile_base + lane
@@ -198,7 +210,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
       const float res = hh ? r[1] : r[0];  // lane l holds key tile_base + l
       if (my_key < wg_end) {
         const int64_t bt = (int64_t)b * T + t0 + t;
-        scores[bt * L + my_key] = my_key < vis[t] ? res * ks : -INFINITY;
+        const float v = res * ks;
+        scores[bt * L + my_key] = my_key < vis[t] ? v : -INFINITY;
+        if (HIST && my_key < vis[t]) atomicAdd(&s_hist[score_key(v) >> 20], 1u);
       }
       // past 4 queries, one query's MFMA results at a time (the scheduler
       // would otherwise hold every query's in registers at once)
@@ -213,16 +227,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
   constexpr int kStride = kWaves * kSuper;
   v8i ta[4], tb[4];
   float ka, kb;
-  load_tile(base, ta, ka);
-  for (;;) {
-    load_tile(base + kStride < wg_end ? base + kStride : base, tb, kb);
-    score_tile(ta, ka, base);
-    base += kStride;
-    if (base >= wg_end) break;
-    load_tile(base + kStride < wg_end ? base + kStride : base, ta, ka);
-    score_tile(tb, kb, base);
-    base += kStride;
-    if (base >= wg_end) break;
+  if (base < wg_end) {
+    load_tile(base, ta, ka);
+    for (;;) {
+      load_tile(base + kStride < wg_end ? base + kStride : base, tb, kb);
+      score_tile(ta, ka, base);
+      base += kStride;
+      if (base >= wg_end) break;
+      load_tile(base + kStride < wg_end ? base + kStride : base, ta, ka);
+      score_tile(tb, kb, base);
+      base += kStride;
+      if (base >= wg_end) break;
+    }
+  }
+  if (HIST) {
+    __syncthreads();
+    uint32_t* rh = hist + (size_t)b * kHistBins;
+    // the thread index rebuilt from the wave index (uniform) and the lane
+    // count, so that no register holds it across the key loop
+    const int tid = (__builtin_amdgcn_readfirstlane(wave) << 6) +
+                    (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    for (int i = tid; i < kHistBins; i += 256) {
+      const uint32_t c = s_hist[i];
+      if (c) atomicAdd(&rh[i], c);
+    }
   }
 }
 
@@ -440,7 +468,7 @@ template <bool PAGED>
 hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float* w,
                            const uint8_t* k8, const float* k_scale, const int32_t* vis_len, int B,
                            int T, int L, float* scores, const int32_t* btab, int max_blocks,
-                           int lbs, int n_blocks, hipStream_t stream) {
+                           int lbs, int n_blocks, uint32_t* hist, hipStream_t stream) {
   if (T >= LCS_IDX_PREFILL_MIN_T) {
     // workgroups: key blocks of 1024 x query ranges x batch, the query ranges
     // (multiples of the 8-query chunk) sized for about 4 workgroups per CU
@@ -462,13 +490,20 @@ hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float*
   if (iters > LCS_IDX_MAX_ITERS) iters = LCS_IDX_MAX_ITERS;
   const int kpw = (int)(iters * kWaves * kSuper);
   dim3 grid((unsigned)((L + kpw - 1) / kpw), (unsigned)B);
+  if (hist) {
+    if (PAGED || T != 1) return hipErrorInvalidValue;
+    return launch_kernel(idx_decode_kernel<1, false, true>, grid, dim3(256), 0, stream, q8,
+                         q_scale, w, k8, k_scale, vis_len, T, 0, L, kpw, scores, btab, max_blocks,
+                         lbs, n_blocks, hist);
+  }
   for (int t0 = 0; t0 < T; t0 += kMaxTq) {
     const int tq = T - t0 < kMaxTq ? T - t0 : kMaxTq;
     hipError_t e;
 #define LCS_DECODE_CASE(N)                                                                      \
   case N:                                                                                       \
     e = launch_kernel(idx_decode_kernel<N, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w, k8, \
-                      k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs, n_blocks);   \
+                      k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs, n_blocks,    \
+                      nullptr);                                                                  \
     break;
     switch (tq) {
       LCS_DECODE_CASE(1)
@@ -479,7 +514,7 @@ hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float*
       default:
         e = launch_kernel(idx_decode_kernel<kMaxTq, PAGED>, grid, dim3(256), 0, stream, q8, q_scale,
                           w, k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
-                          n_blocks);
+                          n_blocks, nullptr);
         break;
     }
 #undef LCS_DECODE_CASE
@@ -494,7 +529,14 @@ hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float
                             const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
                             int B, int T, int L, float* scores, hipStream_t stream) {
   return launch_idx_impl<false>(q8, q_scale, w, k8, k_scale, vis_len, B, T, L, scores, nullptr, 0,
-                                0, 0, stream);
+                                0, 0, nullptr, stream);
+}
+
+hipError_t launch_idx_score_hist(const uint8_t* q8, const float* q_scale, const float* w,
+                                 const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
+                                 int B, int L, float* scores, uint32_t* hist, hipStream_t stream) {
+  return launch_idx_impl<false>(q8, q_scale, w, k8, k_scale, vis_len, B, 1, L, scores, nullptr, 0,
+                                0, 0, hist, stream);
 }
 
 hipError_t launch_idx_score_paged(const uint8_t* q8, const float* q_scale, const float* w,
@@ -503,7 +545,7 @@ hipError_t launch_idx_score_paged(const uint8_t* q8, const float* q_scale, const
                                   int n_blocks, const int32_t* vis_len, int B, int T, int L,
                                   float* scores, hipStream_t stream) {
   return launch_idx_impl<true>(q8, q_scale, w, k8, k_scale, vis_len, B, T, L, scores, block_table,
-                               max_blocks, lbs, n_blocks, stream);
+                               max_blocks, lbs, n_blocks, nullptr, stream);
 }
 
 }  // namespace lcs

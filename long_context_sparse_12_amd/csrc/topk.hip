@@ -290,7 +290,7 @@ constexpr int kStagePer = kStage / kThreads;  // 16 entries per thread
 __global__ void __launch_bounds__(kThreads) topk_final_kernel(
     const float* __restrict__ scores, int L, int k, int chunks, int chunk,
     const RowState* __restrict__ state, const uint32_t* __restrict__ counts,
-    const uint32_t* __restrict__ lists, int32_t* __restrict__ idx) {
+    const uint32_t* __restrict__ lists, int32_t* __restrict__ idx, uint32_t* __restrict__ ghist) {
   __shared__ uint32_t s_wave[2 * kWavesTk];
   __shared__ uint32_t hist[kBins2];
   __shared__ uint32_t s_scan[kThreads + kWavesTk];
@@ -300,6 +300,12 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
   __shared__ uint32_t s_key[kStage];  // their keys (candidates only)
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  // The filter launch has read the row histogram: leave it zero for the next
+  // selection, whose histogram may be accumulated by the indexer launch.
+  {
+    uint4* h = (uint4*)(ghist + (size_t)row * kBins1);
+    for (int i = tid; i < kBins1 / 4; i += kThreads) h[i] = uint4{0u, 0u, 0u, 0u};
+  }
   const RowState st = state[row];
   if (st.b1 == kAll) return;
   const uint32_t b1 = st.b1;
@@ -648,15 +654,36 @@ size_t topk_workspace_bytes(int64_t rows, int L, int /*k*/) {
   return make_layout(rows, L).total;
 }
 
-hipError_t launch_topk(const float* scores, const int32_t* vis_len, int rows, int L, int k,
-                       int32_t* idx, void* workspace, hipStream_t stream) {
-  const Layout ly = make_layout(rows, L);
-  char* ws = (char*)workspace;
+namespace {
+
+// one workgroup per row (topk_row_kernel) or the chunked launches
+bool uses_row_kernel(int64_t rows, int L) { return L <= kRowMaxL && rows >= kRowMinRows; }
+
+// the chunked launches after the row histograms are complete
+hipError_t launch_filter_final(const float* scores, const int32_t* vis_len, int rows, int L, int k,
+                               int32_t* idx, char* ws, const Layout& ly, hipStream_t stream) {
   RowState* state = (RowState*)ws;
   uint32_t* ghist = (uint32_t*)(ws + ly.off_hist);
   uint32_t* counts = (uint32_t*)(ws + ly.off_counts);
   uint32_t* lists = (uint32_t*)(ws + ly.off_lists);
-  if (L <= kRowMaxL && rows >= kRowMinRows)  // one workgroup per row; spills in the list area
+  dim3 grid((unsigned)ly.chunks, (unsigned)rows);
+  hipError_t e = launch_kernel(topk_filter_kernel, grid, dim3(kThreads), 0, stream, scores,
+                               vis_len, L, k, ly.chunks, ly.chunk, state, ghist, counts, lists,
+                               idx);
+  if (e != hipSuccess) return e;
+  return launch_kernel(topk_final_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores,
+                       L, k, ly.chunks, ly.chunk, state, counts, lists, idx, ghist);
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float* scores, const int32_t* vis_len, int rows, int L, int k,
+                       int32_t* idx, void* workspace, hipStream_t stream) {
+  const Layout ly = make_layout(rows, L);
+  char* ws = (char*)workspace;
+  uint32_t* ghist = (uint32_t*)(ws + ly.off_hist);
+  uint32_t* lists = (uint32_t*)(ws + ly.off_lists);
+  if (uses_row_kernel(rows, L))  // one workgroup per row; spills in the list area
     return launch_kernel(topk_row_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores,
                          vis_len, L, k, ly.chunks * ly.chunk, lists, idx);
   dim3 grid((unsigned)ly.chunks, (unsigned)rows);
@@ -668,11 +695,25 @@ hipError_t launch_topk(const float* scores, const int32_t* vis_len, int rows, in
   e = launch_kernel(topk_hist_kernel, grid, dim3(kThreads), 0, stream, scores, vis_len, L, k,
                     ly.chunks, ly.chunk, ghist);
   if (e != hipSuccess) return e;
-  e = launch_kernel(topk_filter_kernel, grid, dim3(kThreads), 0, stream, scores, vis_len, L, k,
-                    ly.chunks, ly.chunk, state, ghist, counts, lists, idx);
-  if (e != hipSuccess) return e;
-  return launch_kernel(topk_final_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores,
-                       L, k, ly.chunks, ly.chunk, state, counts, lists, idx);
+  return launch_filter_final(scores, vis_len, rows, L, k, idx, ws, ly, stream);
+}
+
+bool topk_takes_prebuilt_hist(int64_t rows, int L) { return !uses_row_kernel(rows, L); }
+
+uint32_t* topk_hist_area(void* workspace, int64_t rows, int L) {
+  return (uint32_t*)((char*)workspace + make_layout(rows, L).off_hist);
+}
+
+hipError_t launch_topk_clear(void* workspace, int rows, int L, hipStream_t stream) {
+  return launch_kernel(topk_clear_kernel, dim3((unsigned)rows), dim3(256), 0, stream,
+                       topk_hist_area(workspace, rows, L));
+}
+
+hipError_t launch_topk_prebuilt(const float* scores, const int32_t* vis_len, int rows, int L,
+                                int k, int32_t* idx, void* workspace, hipStream_t stream) {
+  if (!topk_takes_prebuilt_hist(rows, L)) return hipErrorInvalidValue;
+  return launch_filter_final(scores, vis_len, rows, L, k, idx, (char*)workspace,
+                             make_layout(rows, L), stream);
 }
 
 }  // namespace lcs
