@@ -16,14 +16,16 @@
 //           key bits and adds it to the row histogram
 //   filter: every (row, chunk) workgroup derives from the row histogram the
 //           bucket b1 holding the k-th largest key, then writes, in position
-//           order, the positions whose bucket is above b1 ("sure") or equal to
-//           b1 ("candidate") into its slice of the row's list
-//   final : one workgroup per row stages the row's entries and candidate
-//           keys in LDS (up to 16384; more are read from global memory), resolves
-//           the candidates with two more digits (12 + 8 bits), which fixes the
-//           exact threshold key tau and how many keys equal to tau are kept
-//           (the lowest positions), then emits the selection in position order.
-// Scores are read twice plus one gather per candidate.
+//           order, the (position, key) pairs whose bucket is above b1 ("sure")
+//           or equal to b1 ("candidate") into its slice of the row's list
+//   final : one workgroup per row loads the row's entries into registers (32
+//           consecutive entries per thread, up to 16384; longer lists are
+//           re-read from global memory per pass), resolves the candidates with
+//           two more digits (12 + 8 bits), which fixes the exact threshold key
+//           tau and how many keys equal to tau are kept (the lowest positions),
+//           then writes each thread's selected entries at its block prefix of
+//           selection counts, i.e. in position order.
+// Scores are read twice; the lists carry the keys, so no score is gathered.
 #include "common.h"
 
 namespace lcs {
@@ -43,6 +45,14 @@ struct RowState {
   uint32_t n_above;  // keys in buckets above b1
   uint32_t pad0, pad1;
 };
+
+// Many rows of moderate length take one workgroup per row (topk_row_kernel);
+// the others the chunked launches.
+constexpr int kRowMaxL = 1 << 18;
+constexpr int kRowMinRows = 512;
+__host__ __device__ inline bool uses_row_kernel(int64_t rows, int L) {
+  return L <= kRowMaxL && rows >= kRowMinRows;
+}
 
 struct Layout {
   int chunks;
@@ -70,8 +80,11 @@ __host__ __device__ inline Layout make_layout(int64_t rows, int L) {
   ly.off_counts = off;
   off += (size_t)rows * ly.chunks * sizeof(uint32_t);
   off = (off + 255) & ~(size_t)255;
+  // list slots: (entry, key) pairs for the chunked launches, positions only
+  // (the row kernel's spills) otherwise
   ly.off_lists = off;
-  off += (size_t)rows * ly.chunks * (size_t)ly.chunk * sizeof(uint32_t);
+  off += (size_t)rows * ly.chunks * (size_t)ly.chunk *
+         (uses_row_kernel(rows, L) ? sizeof(uint32_t) : sizeof(uint2));
   ly.total = off;
   return ly;
 }
@@ -208,7 +221,7 @@ __global__ void __launch_bounds__(kThreads) topk_hist_kernel(
 __global__ void __launch_bounds__(kThreads) topk_filter_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ vis_len, int L, int k,
     int chunks, int chunk, RowState* __restrict__ state, const uint32_t* __restrict__ ghist,
-    uint32_t* __restrict__ counts, uint32_t* __restrict__ lists, int32_t* __restrict__ idx) {
+    uint32_t* __restrict__ counts, uint2* __restrict__ lists, int32_t* __restrict__ idx) {
   __shared__ uint32_t s_wave[2 * kWavesTk];
   __shared__ uint32_t hist[kBins1];
   __shared__ uint32_t s_scan[kThreads + kWavesTk];
@@ -237,7 +250,7 @@ __global__ void __launch_bounds__(kThreads) topk_filter_kernel(
   if (blockIdx.x == 0 && tid == 0) state[row] = RowState{b1, s_out[1], 0u, 0u};
   // ordered compaction of sure / candidate positions of this chunk
   const float* srow = scores + (size_t)row * L;
-  uint32_t* my = lists + ((size_t)row * chunks + blockIdx.x) * (size_t)chunk;
+  uint2* my = lists + ((size_t)row * chunks + blockIdx.x) * (size_t)chunk;
   uint32_t written = 0;
   int parity = 0;
   // the next block's four scores per thread are loaded before this block's
@@ -256,14 +269,15 @@ __global__ void __launch_bounds__(kThreads) topk_filter_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = nv[j];
     if (base + 4 * kThreads < end) load4(base + 4 * kThreads);
-    uint32_t e[4];
+    uint32_t e[4], key[4];
     uint32_t c = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s = base + 4 * tid + j;
       e[j] = 0;
+      key[j] = score_key(v[j]);
       if (s < end) {
-        const uint32_t d = score_key(v[j]) >> 20;
+        const uint32_t d = key[j] >> 20;
         if (d >= b1) {
           e[j] = (uint32_t)s | (d > b1 ? kSure : 0u) | 0x40000000u;  // bit 30: valid
           ++c;
@@ -275,7 +289,7 @@ __global__ void __launch_bounds__(kThreads) topk_filter_kernel(
     parity ^= 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (e[j]) my[pos++] = e[j] & ~0x40000000u;
+      if (e[j]) my[pos++] = uint2{e[j] & ~0x40000000u, key[j]};
     written += tot;
   }
   if (tid == 0) counts[(size_t)row * chunks + blockIdx.x] = written;
@@ -283,21 +297,33 @@ __global__ void __launch_bounds__(kThreads) topk_filter_kernel(
 
 
 
-// Candidates a row can stage in LDS for the fast path of the final kernel
-constexpr int kStage = 16384;
-constexpr int kStagePer = kStage / kThreads;  // 16 entries per thread
+// Entries a row keeps in registers on the fast path of the final kernel:
+// up to kStagePer per thread.
+constexpr int kStagePer = 32;
+constexpr int kStage = kThreads * kStagePer;  // 16384
+
+// The list entries of a row are the chunks' lists concatenated in chunk
+// (= position) order; entry e of the row is slot e - pref[c] of chunk c, the
+// last chunk with pref[c] <= e.
+__device__ __forceinline__ int chunk_of(const uint32_t* pref, int chunks, uint32_t e) {
+  int lo = 0, hi = chunks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pref[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
 __global__ void __launch_bounds__(kThreads) topk_final_kernel(
-    const float* __restrict__ scores, int L, int k, int chunks, int chunk,
-    const RowState* __restrict__ state, const uint32_t* __restrict__ counts,
-    const uint32_t* __restrict__ lists, int32_t* __restrict__ idx, uint32_t* __restrict__ ghist) {
-  __shared__ uint32_t s_wave[2 * kWavesTk];
+    int k, int chunks, int chunk, const RowState* __restrict__ state,
+    const uint32_t* __restrict__ counts, const uint2* __restrict__ lists,
+    int32_t* __restrict__ idx, uint32_t* __restrict__ ghist) {
   __shared__ uint32_t hist[kBins2];
   __shared__ uint32_t s_scan[kThreads + kWavesTk];
   __shared__ uint32_t s_out[2];
   __shared__ uint32_t s_pref[1024 + 1];
-  __shared__ uint32_t s_ent[kStage];  // entries (position | sure flag), in position order
-  __shared__ uint32_t s_key[kStage];  // their keys (candidates only)
+  __shared__ uint32_t s_src[kStage];  // list slot of each entry (fast path)
+  __shared__ uint32_t s_wtot[2][kWavesTk];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   // The filter launch has read the row histogram: leave it zero for the next
@@ -306,12 +332,12 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
     uint4* h = (uint4*)(ghist + (size_t)row * kBins1);
     for (int i = tid; i < kBins1 / 4; i += kThreads) h[i] = uint4{0u, 0u, 0u, 0u};
   }
+  for (int i = tid; i < kBins2; i += kThreads) hist[i] = 0;
   const RowState st = state[row];
   if (st.b1 == kAll) return;
   const uint32_t b1 = st.b1;
-  const float* srow = scores + (size_t)row * L;
   int32_t* out = idx + (size_t)row * k;
-  const uint32_t* list = lists + (size_t)row * chunks * (size_t)chunk;
+  const uint2* list = lists + (size_t)row * chunks * (size_t)chunk;
   // chunk offsets in the concatenated entry list (chunks <= 2 * kThreads)
   {
     const int c0 = 2 * tid;
@@ -325,135 +351,151 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
     __syncthreads();
   }
   const uint32_t n_ent = s_pref[chunks];
-  const uint32_t n_above = st.n_above;
-  auto chunk_of = [&](uint32_t e) -> int {
-    int lo = 0, hi = chunks - 1;  // last chunk with s_pref[c] <= e
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pref[mid] <= e) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  };
-  auto entry = [&](uint32_t e) -> uint32_t {
-    const int c = chunk_of(e);
-    return list[(size_t)c * chunk + (e - s_pref[c])];
-  };
-  const bool staged = n_ent <= (uint32_t)kStage;
-  if (staged) {
-    // Stage every entry and candidate key in LDS with all global loads of a
-    // thread in flight together (one latency for the entries, one for keys).
-    // The source offset of every entry is first written chunk by chunk into
-    // s_key (LDS only), then read back by entry.
+  const uint32_t need1 = (uint32_t)k - st.n_above;
+
+  if (n_ent <= (uint32_t)kStage) {
+    // Fast path: wave w holds entries [w 64 R, (w + 1) 64 R), lane l those
+    // with e = w 64 R + 64 j + l (j < R <= kStagePer), with their keys, in
+    // registers. Consecutive entries of a chunk are consecutive in memory, so
+    // the loads are coalesced; their sources come from an LDS table.
     for (int c = tid; c < chunks; c += kThreads) {
       const uint32_t p0 = s_pref[c], n = s_pref[c + 1] - p0;
-      for (uint32_t i = 0; i < n; ++i) s_key[p0 + i] = (uint32_t)c * chunk + i;
+      for (uint32_t i = 0; i < n; ++i) s_src[p0 + i] = (uint32_t)c * chunk + i;
     }
     __syncthreads();
-    uint32_t v[kStagePer];
+    const int wave = tid >> 6, lane = tid & 63;
+    const uint32_t R = (n_ent + kThreads - 1) / kThreads;
+    const uint32_t wbase = (uint32_t)wave * 64u * R;
+    // (the loaded values are not touched here, so that no wait separates
+    // the loads; bit j of vmask says whether slot j holds an entry)
+    uint32_t ent[kStagePer], key[kStagePer], vmask = 0;
 #pragma unroll
     for (int j = 0; j < kStagePer; ++j) {
-      const uint32_t e = tid + kThreads * j;
-      v[j] = e < n_ent ? list[s_key[e]] : 0u;
-    }
-    float f[kStagePer];
-#pragma unroll
-    for (int j = 0; j < kStagePer; ++j) {
-      const uint32_t e = tid + kThreads * j;
-      f[j] = (e < n_ent && !(v[j] & kSure)) ? srow[v[j] & ~kSure] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < kStagePer; ++j) {
-      const uint32_t e = tid + kThreads * j;
-      if (e < n_ent) {
-        s_ent[e] = v[j];
-        s_key[e] = score_key(f[j]);
+      const uint32_t e = wbase + 64u * j + lane;
+      ent[j] = 0u;
+      key[j] = 0u;
+      if ((uint32_t)j < R && e < n_ent) {
+        const uint2 v = list[s_src[e]];
+        ent[j] = v.x;
+        key[j] = v.y;
+        vmask |= 1u << j;
       }
     }
-  }
-  // entry e and its key (valid for candidates only)
-  auto get = [&](uint32_t e, uint32_t& key) -> uint32_t {
-    if (staged) {
-      key = s_key[e];
-      return s_ent[e];
+    auto cand = [&](int j) { return ((vmask >> j) & 1u) && !(ent[j] & kSure); };
+    // digit 2 (key bits 19..8) over the candidates
+#pragma unroll
+    for (int j = 0; j < kStagePer; ++j)
+      if (cand(j)) atomicAdd(&hist[(key[j] >> 8) & 0xFFFu], 1u);
+    __syncthreads();
+    select_bucket<kBins2>(hist, need1, s_scan, s_out);
+    const uint32_t b2 = s_out[0];
+    const uint32_t above2 = s_out[1];
+    for (int i = tid; i < kBins3; i += kThreads) hist[i] = 0;
+    __syncthreads();
+    // digit 3 (key bits 7..0) over the candidates inside bucket b2
+    const uint32_t pre12 = (b1 << 12) | b2;
+#pragma unroll
+    for (int j = 0; j < kStagePer; ++j)
+      if (cand(j) && (key[j] >> 8) == pre12)
+        atomicAdd(&hist[key[j] & 0xFFu], 1u);
+    __syncthreads();
+    const uint32_t need2 = need1 - above2;
+    select_bucket<kBins3>(hist, need2, s_scan, s_out);
+    const uint32_t b3 = s_out[0];
+    const uint32_t tau = (pre12 << 8) | b3;
+    const uint32_t need_tie = need2 - s_out[1];  // keys equal to tau that are kept
+    // Ties need ranks only when some of them are dropped.
+    const bool rank_ties = need_tie < hist[b3];
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // entries of this wave before this one (in entry order) that are ties
+    uint32_t tie_run = 0;
+    if (rank_ties) {
+      uint32_t wt = 0;
+#pragma unroll
+      for (int j = 0; j < kStagePer; ++j)
+        if ((uint32_t)j < R)
+          wt += (uint32_t)__popcll(__ballot(cand(j) && key[j] == tau));
+      if (lane == 0) s_wtot[0][wave] = wt;
+      __syncthreads();
+      for (int i = 0; i < wave; ++i) tie_run += s_wtot[0][i];
     }
-    const uint32_t v = entry(e);
-    key = (v & kSure) ? 0u : score_key(srow[v]);
-    return v;
+    // keep flags, in entry order
+    uint32_t sel = 0, wsel = 0;
+#pragma unroll
+    for (int j = 0; j < kStagePer; ++j) {
+      if ((uint32_t)j >= R) continue;
+      const bool valid = (vmask >> j) & 1u;
+      const bool sure = valid && (ent[j] & kSure);
+      const bool tie = valid && !sure && key[j] == tau;
+      bool keep = valid && (sure || key[j] > tau);
+      if (rank_ties) {
+        const uint64_t tm = __ballot(tie);
+        if (tie) keep = tie_run + (uint32_t)__popcll(tm & lt) < need_tie;
+        tie_run += (uint32_t)__popcll(tm);
+      } else if (tie) {
+        keep = true;
+      }
+      sel |= (keep ? 1u : 0u) << j;
+      wsel += (uint32_t)__popcll(__ballot(keep));
+    }
+    // this wave's output offset: the selections of the waves before it
+    if (lane == 0) s_wtot[1][wave] = wsel;
+    __syncthreads();
+    uint32_t pos = 0;
+    for (int i = 0; i < wave; ++i) pos += s_wtot[1][i];
+#pragma unroll
+    for (int j = 0; j < kStagePer; ++j) {
+      if ((uint32_t)j >= R) continue;
+      const bool keep = (sel >> j) & 1u;
+      const uint64_t km = __ballot(keep);
+      const uint32_t p = pos + (uint32_t)__popcll(km & lt);
+      if (keep && p < (uint32_t)k) out[p] = (int32_t)(ent[j] & ~kSure);
+      pos += (uint32_t)__popcll(km);
+    }
+    return;
+  }
+
+  // Slow path (more entries than the registers hold): every pass reads the
+  // entries from the lists again.
+  auto entry = [&](uint32_t e) -> uint2 {
+    const int c = chunk_of(s_pref, chunks, e);
+    return list[(size_t)c * chunk + (e - s_pref[c])];
   };
-  // digit 2 over the candidates
-  for (int i = tid; i < kBins2; i += kThreads) hist[i] = 0;
-  __syncthreads();
   for (uint32_t e = tid; e < n_ent; e += kThreads) {
-    uint32_t key;
-    const uint32_t v = get(e, key);
-    if (!(v & kSure)) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
+    const uint2 v = entry(e);
+    if (!(v.x & kSure)) atomicAdd(&hist[(v.y >> 8) & 0xFFFu], 1u);
   }
   __syncthreads();
-  const uint32_t need1 = (uint32_t)k - n_above;
   select_bucket<kBins2>(hist, need1, s_scan, s_out);
   const uint32_t b2 = s_out[0];
   const uint32_t above2 = s_out[1];
-  __syncthreads();
-  // digit 3 over the candidates inside bucket b2
   for (int i = tid; i < kBins3; i += kThreads) hist[i] = 0;
   __syncthreads();
   const uint32_t pre12 = (b1 << 12) | b2;
   for (uint32_t e = tid; e < n_ent; e += kThreads) {
-    uint32_t key;
-    const uint32_t v = get(e, key);
-    if (!(v & kSure) && (key >> 8) == pre12) atomicAdd(&hist[key & 0xFFu], 1u);
+    const uint2 v = entry(e);
+    if (!(v.x & kSure) && (v.y >> 8) == pre12) atomicAdd(&hist[v.y & 0xFFu], 1u);
   }
   __syncthreads();
   const uint32_t need2 = need1 - above2;
   select_bucket<kBins3>(hist, need2, s_scan, s_out);
   const uint32_t b3 = s_out[0];
-  const uint32_t above3 = s_out[1];
   const uint32_t tau = (pre12 << 8) | b3;
-  const uint32_t need_tie = need2 - above3;  // keys equal to tau that are kept
-  __syncthreads();
-  // ordered emission, four consecutive entries per thread per block
+  const uint32_t need_tie = need2 - s_out[1];
+  // ordered emission, one entry per thread per round
   uint32_t ties_before = 0, sel_before = 0;
-  int parity = 0;
-  for (uint32_t base = 0; base < n_ent; base += 4 * kThreads) {
-    uint32_t pos4[4], gt4[4], tie4[4];
-    uint32_t n_tie = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t e = base + 4 * tid + j;
-      gt4[j] = tie4[j] = 0;
-      pos4[j] = 0;
-      if (e < n_ent) {
-        uint32_t key;
-        const uint32_t v = get(e, key);
-        pos4[j] = v & ~kSure;
-        if (v & kSure) {
-          gt4[j] = 1;
-        } else {
-          gt4[j] = key > tau;
-          tie4[j] = key == tau;
-        }
-      }
-      n_tie += tie4[j];
-    }
+  for (uint32_t base = 0; base < n_ent; base += kThreads) {
+    const uint32_t e = base + tid;
+    uint2 v = uint2{0u, 0u};
+    if (e < n_ent) v = entry(e);
+    const bool valid = e < n_ent;
+    const bool tie = valid && !(v.x & kSure) && v.y == tau;
     uint32_t tie_tot;
-    uint32_t tie_rank = ties_before + block_prefix_small(n_tie, s_wave, parity, tie_tot);
-    parity ^= 1;
-    uint32_t sel4[4], n_sel = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sel4[j] = gt4[j] | (tie4[j] & (tie_rank < need_tie ? 1u : 0u));
-      tie_rank += tie4[j];
-      n_sel += sel4[j];
-    }
+    const uint32_t tie_rank = ties_before + block_prefix(tie ? 1u : 0u, s_scan, tie_tot);
+    const bool keep = valid && ((v.x & kSure) || (!tie && v.y > tau) || (tie && tie_rank < need_tie));
     uint32_t sel_tot;
-    uint32_t pos = sel_before + block_prefix_small(n_sel, s_wave, parity, sel_tot);
-    parity ^= 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (sel4[j]) {
-        if (pos < (uint32_t)k) out[pos] = (int32_t)pos4[j];
-        ++pos;
-      }
+    const uint32_t pos = sel_before + block_prefix(keep ? 1u : 0u, s_scan, sel_tot);
+    if (keep && pos < (uint32_t)k) out[pos] = (int32_t)(v.x & ~kSure);
     ties_before += tie_tot;
     sel_before += sel_tot;
   }
@@ -474,8 +516,6 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
 // keeps at most ~64 KB of loads in flight, so the row kernel pays only where
 // many rows fill the chip (chunked prefill); a few long rows (decode) use the
 // chunked launches, which spread each row over many CUs.
-constexpr int kRowMaxL = 1 << 18;
-constexpr int kRowMinRows = 512;
 constexpr int kRowCap = 2048;  // LDS list entries per wave (8 waves: 16384)
 
 __global__ void __launch_bounds__(kThreads) topk_row_kernel(
@@ -656,8 +696,6 @@ size_t topk_workspace_bytes(int64_t rows, int L, int /*k*/) {
 
 namespace {
 
-// one workgroup per row (topk_row_kernel) or the chunked launches
-bool uses_row_kernel(int64_t rows, int L) { return L <= kRowMaxL && rows >= kRowMinRows; }
 
 // the chunked launches after the row histograms are complete
 hipError_t launch_filter_final(const float* scores, const int32_t* vis_len, int rows, int L, int k,
@@ -665,14 +703,14 @@ hipError_t launch_filter_final(const float* scores, const int32_t* vis_len, int 
   RowState* state = (RowState*)ws;
   uint32_t* ghist = (uint32_t*)(ws + ly.off_hist);
   uint32_t* counts = (uint32_t*)(ws + ly.off_counts);
-  uint32_t* lists = (uint32_t*)(ws + ly.off_lists);
+  uint2* lists = (uint2*)(ws + ly.off_lists);
   dim3 grid((unsigned)ly.chunks, (unsigned)rows);
   hipError_t e = launch_kernel(topk_filter_kernel, grid, dim3(kThreads), 0, stream, scores,
                                vis_len, L, k, ly.chunks, ly.chunk, state, ghist, counts, lists,
                                idx);
   if (e != hipSuccess) return e;
-  return launch_kernel(topk_final_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, scores,
-                       L, k, ly.chunks, ly.chunk, state, counts, lists, idx, ghist);
+  return launch_kernel(topk_final_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, k,
+                       ly.chunks, ly.chunk, state, counts, lists, idx, ghist);
 }
 
 }  // namespace
