@@ -37,6 +37,10 @@ constexpr int kBins1 = 4096;  // key bits 31..20
 constexpr int kBins2 = 4096;  // key bits 19..8
 constexpr int kBins3 = 256;   // key bits 7..0
 constexpr int kMinChunk = 2048;
+#ifndef LCS_TOPK_MAX_CHUNK
+#define LCS_TOPK_MAX_CHUNK 8192
+#endif
+constexpr int64_t kMaxChunkAim = LCS_TOPK_MAX_CHUNK;
 constexpr uint32_t kAll = 0xFFFFFFFFu;  // state.b1 marker: keep every visible position
 constexpr uint32_t kSure = 0x80000000u;
 
@@ -62,8 +66,11 @@ struct Layout {
 
 __host__ __device__ inline Layout make_layout(int64_t rows, int L) {
   Layout ly;
-  // aim for >= ~1024 workgroups per launch
+  // aim for >= ~1024 workgroups per launch, and chunks of at most
+  // kMaxChunkAim positions where that gives more
   int64_t want = (1024 + rows - 1) / rows;
+  const int64_t by_len = (L + kMaxChunkAim - 1) / kMaxChunkAim;
+  if (by_len > want) want = by_len;
   int64_t max_chunks = (L + kMinChunk - 1) / kMinChunk;
   if (want > max_chunks) want = max_chunks;
   if (want > 1024) want = 1024;
