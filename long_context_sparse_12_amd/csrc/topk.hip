@@ -523,7 +523,13 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
 // keeps at most ~64 KB of loads in flight, so the row kernel pays only where
 // many rows fill the chip (chunked prefill); a few long rows (decode) use the
 // chunked launches, which spread each row over many CUs.
-constexpr int kRowCap = 2048;  // LDS list entries per wave (8 waves: 16384)
+constexpr int kRowCap = 2048;
+#ifndef LCS_ROW_PER1
+#define LCS_ROW_PER1 16  // scores per thread per step of the histogram pass
+#endif
+#ifndef LCS_ROW_PER2
+#define LCS_ROW_PER2 16  // scores per lane per step of the compaction pass
+#endif  // LDS list entries per wave (8 waves: 16384)
 
 __global__ void __launch_bounds__(kThreads) topk_row_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ vis_len, int L, int k,
@@ -548,17 +554,33 @@ __global__ void __launch_bounds__(kThreads) topk_row_kernel(
   // ---- pass 1: histogram of key bits 31..20 ----
   for (int i = tid; i < kBins1; i += kThreads) hist[i] = 0;
   __syncthreads();
-  constexpr int kPer = 32;  // loads of a thread in flight before its atomics
-  for (int base = 0; base < vis; base += kThreads * kPer) {
-    float v[kPer];
+  // kPer loads of a thread per step, in two register buffers used in turn:
+  // the next step's loads are issued before this step's atomics, so two
+  // steps are in flight. The loads are unconditional (positions past the end
+  // read the row's last score, vis >= 2 here, and are not counted), so the
+  // wait before a step's atomics covers that step's loads only.
+  constexpr int kPer = LCS_ROW_PER1;
+  constexpr int kStep1 = kThreads * kPer;
+  float va[kPer], vb[kPer];
+  auto load1 = [&](float (&v)[kPer], int base) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int p = base + kThreads * j + tid;
-      v[j] = p < vis ? srow[p] : 0.f;
-    }
+    for (int j = 0; j < kPer; ++j) v[j] = srow[min(base + kThreads * j + tid, vis - 1)];
+  };
+  auto count1 = [&](const float (&v)[kPer], int base) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (base + kThreads * j + tid < vis) atomicAdd(&hist[score_key(v[j]) >> 20], 1u);
+  };
+  load1(va, 0);
+  for (int base = 0;;) {
+    load1(vb, base + kStep1);
+    count1(va, base);
+    base += kStep1;
+    if (base >= vis) break;
+    load1(va, base + kStep1);
+    count1(vb, base);
+    base += kStep1;
+    if (base >= vis) break;
   }
   __syncthreads();
   select_bucket<kBins1>(hist, (uint32_t)k, s_scan, s_out);
@@ -572,14 +594,16 @@ __global__ void __launch_bounds__(kThreads) topk_row_kernel(
   uint32_t* my_spill = spill + (size_t)row * spill_stride + (size_t)wave * seg_cap;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   uint32_t cnt = 0;
-  constexpr int kPer2 = 16;  // loads of a lane in flight per step
-  for (int base = p0; base < p1; base += kPer2 * 64) {
-    float v[kPer2];
+  // kPer2 loads of a lane per step, in two register buffers used in turn as
+  // in pass 1 (positions past the segment read a valid score, not kept)
+  constexpr int kPer2 = LCS_ROW_PER2;
+  constexpr int kStep2 = 64 * kPer2;
+  float wa[kPer2], wb[kPer2];
+  auto load2 = [&](float (&v)[kPer2], int base) {
 #pragma unroll
-    for (int j = 0; j < kPer2; ++j) {
-      const int p = base + 64 * j + lane;
-      v[j] = p < p1 ? srow[p] : 0.f;
-    }
+    for (int j = 0; j < kPer2; ++j) v[j] = srow[min(base + 64 * j + lane, vis - 1)];
+  };
+  auto compact2 = [&](const float (&v)[kPer2], int base) {
 #pragma unroll
     for (int j = 0; j < kPer2; ++j) {
       const int p = base + 64 * j + lane;
@@ -597,6 +621,19 @@ __global__ void __launch_bounds__(kThreads) topk_row_kernel(
         }
       }
       cnt += (uint32_t)__popcll(m);
+    }
+  };
+  if (p0 < p1) {
+    load2(wa, p0);
+    for (int base = p0;;) {
+      load2(wb, base + kStep2);
+      compact2(wa, base);
+      base += kStep2;
+      if (base >= p1) break;
+      load2(wa, base + kStep2);
+      compact2(wb, base);
+      base += kStep2;
+      if (base >= p1) break;
     }
   }
   if (lane == 0) s_cnt[wave] = cnt;
