@@ -283,6 +283,27 @@ def time_context_parallel(w, lcs, G=8, n=50):
     return res
 
 
+def copy_peak_gbs(mb=1024, n=10):
+    """Measured device-to-device copy bandwidth, bytes read + written per second
+    (a torch copy of `mb` MiB, n times between HIP events after two warm-up
+    copies): the practical HBM ceiling the kernels are also compared with."""
+    import torch
+    src = torch.ones(mb << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / n
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * (mb << 20) / sec / 1e9
+
+
 def time_paged(s, lcs, bs=64, n=20):
     """One full layer of the workload with its keys and latent rows laid out in
     pools of bs-row blocks, the blocks in a random order, against the same
@@ -452,11 +473,14 @@ def main():
         else:
             launch_bytes = w.B * w.L * IDX_BYTES_PER_KEY + w.B * w.T * IDX_BYTES_PER_QUERY
             achieved = launch_bytes / (idx_us * 1e-6) / 1e9
+            cp = copy_peak_gbs()
             res["roofline"] = {"kernel": "idx_score (decode indexer)", "bound": "hbm",
                                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                                "traffic": traffic, "bytes_per_launch": launch_bytes,
-                               "avg_launch_us": round(idx_us, 2)}
+                               "avg_launch_us": round(idx_us, 2),
+                               "copy_peak_measured": round(cp, 1),
+                               "frac_of_copy_peak": round(achieved / cp, 4)}
         res["kernels_us"] = {k: round(v, 2) for k, v in ker.items()}
         res["launches_per_step"] = {k: v // max(args.steps // 2, 3) for k, v in counts.items()}
         ap_us, ap_bytes = time_cache_append(w, lcs, 50)
