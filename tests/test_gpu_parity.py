@@ -428,6 +428,109 @@ def test_composite_fused_histogram_matches_separate_calls():
             assert bad.size == 0, (l, bad[:5])
 
 
+def test_composite_decode128k_full_size_sampled():
+    """The 128K decode group at full size (B=32, T=1, L=131072, layer 0 full,
+    layers 1-3 reuse its selection, bf16 KV) through lcs_indexshare_forward in
+    the benchmark's launch configuration (one query per sequence, so the
+    indexer also builds the top-k histogram). Sampled sequences against the
+    oracle: the selection under the gap rule, and every layer's output and
+    lse over the selection the GPU made."""
+    w = wl.WORKLOADS["decode128k"]
+    _say("case: composite full size %s" % w.name)
+    B, T, L, k = w.B, w.T, w.L, w.k
+    full = w.full_layers()
+    assert full == [0]
+    layers = []
+    for l in range(w.n_layers):
+        d = wl.dev_indexer(w, l, DEV) if l in full else {}
+        d["q"] = wl.dev_attn_q(w, l, DEV)
+        kv, sc = wl.dev_kv(w, l, DEV)
+        d["kv"] = kv
+        if sc is not None:
+            d["kv_scale"] = sc
+        d["out"] = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+        d["lse"] = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+        layers.append(d)
+    vis = w.vis_len()
+    idx_out = torch.empty((len(full), B, T, k), dtype=torch.int32, device=DEV)
+    scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+    ws = _zeros(lcs.indexshare_workspace_bytes(B, T, L, k))
+    lcs.indexshare_forward(layers, lcs.SCHED_GROUP4, to_dev(vis), k, w.sm_scale, scores, idx_out,
+                           ws, kv_dtype=lcs.KV_BF16)
+    torch.cuda.synchronize()
+    got = idx_out.cpu().numpy()
+    for b in (0, 19, 31):
+        inp = wl.host_indexer(w, 0, b0=b, nb=1)
+        s32, s64 = oracle.idx_score(inp["q8"], inp["q_scale"], inp["w"], inp["k8"],
+                                    inp["k_scale"], vis[b:b + 1], want64=True)
+        ref_idx = oracle.topk(s32, vis[b:b + 1], k)
+        ov, gap = check_selection(got[0, b:b + 1], ref_idx, s64)
+        _say("  b=%d selection overlap %.5f worst gap %.3g" % (b, ov, gap))
+        sel = got[0, b, 0]
+        idx_s = np.arange(k, dtype=np.int32).reshape(1, 1, k)
+        for l in range(w.n_layers):
+            q_h = wl.host_attn_q(w, l, b0=b, nb=1)
+            kv_s, sc_s = wl.host_kv_rows(w, l, b, sel)
+            _, ref_lse, ref64 = oracle.sparse_mla(q_h, kv_s, sc_s, idx_s, w.sm_scale, want64=True)
+            mx, _, lerr = check_attention(layers[l]["out"][b:b + 1], ref64,
+                                          layers[l]["lse"][b:b + 1], ref_lse.astype(np.float64))
+            _say("  b=%d layer %d max-abs %.3g, lse err %.3g" % (b, l, mx, lerr))
+    del layers, scores, ws
+    torch.cuda.empty_cache()
+
+
+def test_composite_decode1m_full_size_sampled():
+    """The 1M decode schedule at full size (B=2, T=1, L=2^20, 78 layers, 21
+    full under the GLM-5.2 schedule, E4M3 KV) through lcs_indexshare_forward
+    as the benchmark launches it. Sequence 1 against the oracle: the
+    selections of full layers 0 and 74 (the first and the last: the fused
+    histogram restarted from zero 20 times in between) under the gap rule,
+    and the outputs of layers 0, 1, 74 and 77 over the GPU's selections."""
+    w = wl.WORKLOADS["decode1m"]
+    _say("case: composite full size %s" % w.name)
+    B, T, L, k = w.B, w.T, w.L, w.k
+    full = w.full_layers()
+    assert len(full) == 21 and full[-1] == 74
+    layers = []
+    for l in range(w.n_layers):
+        d = wl.dev_indexer(w, l, DEV) if l in full else {}
+        d["q"] = wl.dev_attn_q(w, l, DEV)
+        kv, sc = wl.dev_kv(w, l, DEV)
+        d["kv"], d["kv_scale"] = kv, sc
+        d["out"] = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+        d["lse"] = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+        layers.append(d)
+    vis = w.vis_len()
+    idx_out = torch.empty((len(full), B, T, k), dtype=torch.int32, device=DEV)
+    scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+    ws = _zeros(lcs.indexshare_workspace_bytes(B, T, L, k))
+    lcs.indexshare_forward(layers, lcs.SCHED_GLM52, to_dev(vis), k, w.sm_scale, scores, idx_out,
+                           ws, kv_dtype=lcs.KV_FP8_E4M3)
+    torch.cuda.synchronize()
+    got = idx_out.cpu().numpy()
+    b = 1
+    for f in (0, 20):
+        l = full[f]
+        inp = wl.host_indexer(w, l, b0=b, nb=1)
+        s32, s64 = oracle.idx_score(inp["q8"], inp["q_scale"], inp["w"], inp["k8"],
+                                    inp["k_scale"], vis[b:b + 1], want64=True)
+        ref_idx = oracle.topk(s32, vis[b:b + 1], k)
+        ov, gap = check_selection(got[f, b:b + 1], ref_idx, s64)
+        _say("  layer %d selection overlap %.5f worst gap %.3g" % (l, ov, gap))
+    idx_s = np.arange(k, dtype=np.int32).reshape(1, 1, k)
+    for l in (0, 1, 74, 77):
+        f = sum(1 for x in full if x <= l) - 1
+        sel = got[f, b, 0]
+        q_h = wl.host_attn_q(w, l, b0=b, nb=1)
+        kv_s, sc_s = wl.host_kv_rows(w, l, b, sel)
+        _, ref_lse, ref64 = oracle.sparse_mla(q_h, kv_s, sc_s, idx_s, w.sm_scale, want64=True)
+        mx, _, lerr = check_attention(layers[l]["out"][b:b + 1], ref64,
+                                      layers[l]["lse"][b:b + 1], ref_lse.astype(np.float64))
+        _say("  layer %d max-abs %.3g, lse err %.3g" % (l, mx, lerr))
+    del layers, scores, ws
+    torch.cuda.empty_cache()
+
+
 def test_mtp_draft_reuse_small():
     w = wl.Workload("mtp-small", seed=22, B=3, T=1, L=7000, n_layers=7, kv_fp8=True, mtp_steps=7)
     _say("case: composite %s" % w.name)
