@@ -531,6 +531,70 @@ def test_composite_decode1m_full_size_sampled():
     torch.cuda.empty_cache()
 
 
+def test_composite_prefill_and_mtp_full_size_sampled():
+    """The chunked prefill (B=1, T=4096 causal queries, L=131072, 4 layers,
+    bf16 KV; the top-k takes the one-workgroup-per-row kernel) and the MTP
+    draft round (B=8, L=2^20, 7 steps on step 0's selection and KV, E4M3) at
+    full size through lcs_indexshare_forward as the benchmark launches them;
+    sampled queries against the oracle as in the decode tests."""
+    for name, sched, mtp, samples, att_layers in (
+            ("prefill", lcs.SCHED_GROUP4, 0, ((0, 0), (0, 1500), (0, 4095)), (0, 3)),
+            ("mtp1m", 0, 7, ((3, 0),), (0, 6))):
+        w = wl.WORKLOADS[name]
+        _say("case: composite full size %s" % w.name)
+        B, T, L, k = w.B, w.T, w.L, w.k
+        n = w.n_layers
+        layers = []
+        for l in range(n):
+            li = w.indexer_layer(l)
+            d = wl.dev_indexer(w, l, DEV) if l in w.full_layers() else {}
+            d["q"] = wl.dev_attn_q(w, l, DEV)
+            if li == l:
+                kv, sc = wl.dev_kv(w, l, DEV)
+                d["kv"] = kv
+                if sc is not None:
+                    d["kv_scale"] = sc
+            d["out"] = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+            d["lse"] = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+            layers.append(d)
+        vis = w.vis_len()
+        n_full = lcs.count_full_layers(sched, n, None, mtp)
+        idx_out = torch.empty((n_full, B, T, k), dtype=torch.int32, device=DEV)
+        scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+        ws = _zeros(lcs.indexshare_workspace_bytes(B, T, L, k))
+        lcs.indexshare_forward(layers, sched, to_dev(vis), k, w.sm_scale, scores, idx_out, ws,
+                               kv_dtype=lcs.KV_FP8_E4M3 if w.kv_fp8 else lcs.KV_BF16,
+                               mtp_steps=mtp)
+        torch.cuda.synchronize()
+        got = idx_out.cpu().numpy()
+        idx_s = np.arange(k, dtype=np.int32).reshape(1, 1, k)
+        for b, t in samples:
+            inp = wl.host_indexer(w, 0, b0=b, nb=1)
+            q_sl = (slice(None), slice(t, t + 1))
+            s32, s64 = oracle.idx_score(inp["q8"][q_sl], inp["q_scale"][q_sl], inp["w"][q_sl],
+                                        inp["k8"], inp["k_scale"], vis[b:b + 1, t:t + 1],
+                                        want64=True)
+            ref_idx = oracle.topk(s32, vis[b:b + 1, t:t + 1], k)
+            ov, gap = check_selection(got[0, b:b + 1, t:t + 1], ref_idx, s64)
+            _say("  b=%d t=%d selection overlap %.5f worst gap %.3g" % (b, t, ov, gap))
+            sel = got[0, b, t]
+            kv_s, sc_s = wl.host_kv_rows(w, 0, b, sel[sel >= 0])
+            idx_v = np.full((1, 1, k), -1, np.int32)
+            idx_v[0, 0, :int((sel >= 0).sum())] = np.arange(int((sel >= 0).sum()), dtype=np.int32)
+            for l in att_layers:
+                if not mtp:
+                    kv_s, sc_s = wl.host_kv_rows(w, l, b, sel[sel >= 0])
+                q_h = wl.host_attn_q(w, l, b0=b, nb=1)[:, t:t + 1]
+                _, ref_lse, ref64 = oracle.sparse_mla(q_h, kv_s, sc_s, idx_v, w.sm_scale,
+                                                      want64=True)
+                mx, _, lerr = check_attention(layers[l]["out"][b:b + 1, t:t + 1], ref64,
+                                              layers[l]["lse"][b:b + 1, t:t + 1],
+                                              ref_lse.astype(np.float64))
+                _say("  b=%d t=%d layer %d max-abs %.3g, lse err %.3g" % (b, t, l, mx, lerr))
+        del layers, scores, ws, idx_out
+        torch.cuda.empty_cache()
+
+
 def test_mtp_draft_reuse_small():
     w = wl.Workload("mtp-small", seed=22, B=3, T=1, L=7000, n_layers=7, kv_fp8=True, mtp_steps=7)
     _say("case: composite %s" % w.name)
