@@ -153,8 +153,8 @@ __device__ uint32_t block_prefix(uint32_t v, uint32_t* s_tmp, uint32_t& tot) {
 }
 
 // Find bucket b of hist[nb] (LDS) with  above(b) < need <= above(b) + hist[b],
-// where above(b) = sum of hist over buckets > b. Result in s_out[0] (bucket)
-// and s_out[1] (above). Requires sum(hist) >= need >= 1. Thread t sums buckets
+// where above(b) = sum of hist over buckets > b. Result in s_out[0] (bucket),
+// s_out[1] (above) and s_out[2] (hist[b]). Requires sum(hist) >= need >= 1. Thread t sums buckets
 // [t BPT, (t + 1) BPT); a block prefix of those sums (shuffles in each wave,
 // the wave totals through LDS) gives every thread the count above its range.
 template <int NB>
@@ -179,6 +179,7 @@ __device__ void select_bucket(const uint32_t* hist, uint32_t need, uint32_t* s_s
       if (run + h >= need) {
         s_out[0] = (uint32_t)bin;
         s_out[1] = run;
+        s_out[2] = h;
         break;
       }
       run += h;
@@ -232,7 +233,7 @@ __global__ void __launch_bounds__(kThreads) topk_filter_kernel(
   __shared__ uint32_t s_wave[2 * kWavesTk];
   __shared__ uint32_t hist[kBins1];
   __shared__ uint32_t s_scan[kThreads + kWavesTk];
-  __shared__ uint32_t s_out[2];
+  __shared__ uint32_t s_out[3];
   const int row = blockIdx.y;
   const int tid = threadIdx.x;
   const int vis = clamp_vis(vis_len[row], L);
@@ -327,7 +328,7 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
     int32_t* __restrict__ idx, uint32_t* __restrict__ ghist) {
   __shared__ uint32_t hist[kBins2];
   __shared__ uint32_t s_scan[kThreads + kWavesTk];
-  __shared__ uint32_t s_out[2];
+  __shared__ uint32_t s_out[3];
   __shared__ uint32_t s_pref[1024 + 1];
   __shared__ uint32_t s_src[kStage];  // list slot of each entry (fast path)
   __shared__ uint32_t s_wtot[2][kWavesTk];
@@ -397,22 +398,31 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
     select_bucket<kBins2>(hist, need1, s_scan, s_out);
     const uint32_t b2 = s_out[0];
     const uint32_t above2 = s_out[1];
-    for (int i = tid; i < kBins3; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    // digit 3 (key bits 7..0) over the candidates inside bucket b2
-    const uint32_t pre12 = (b1 << 12) | b2;
-#pragma unroll
-    for (int j = 0; j < kStagePer; ++j)
-      if (cand(j) && (key[j] >> 8) == pre12)
-        atomicAdd(&hist[key[j] & 0xFFu], 1u);
-    __syncthreads();
     const uint32_t need2 = need1 - above2;
-    select_bucket<kBins3>(hist, need2, s_scan, s_out);
-    const uint32_t b3 = s_out[0];
-    const uint32_t tau = (pre12 << 8) | b3;
-    const uint32_t need_tie = need2 - s_out[1];  // keys equal to tau that are kept
-    // Ties need ranks only when some of them are dropped.
-    const bool rank_ties = need_tie < hist[b3];
+    const uint32_t pre12 = (b1 << 12) | b2;
+    // tau: the smallest kept key; keys equal to tau past the first need_tie
+    // are dropped, which needs tie ranks only when some are dropped
+    uint32_t tau, need_tie;
+    bool rank_ties;
+    if (s_out[2] == need2) {
+      // every candidate of bucket b2 is kept: no third digit
+      tau = pre12 << 8;
+      need_tie = 0;
+      rank_ties = false;
+    } else {
+      for (int i = tid; i < kBins3; i += kThreads) hist[i] = 0;
+      __syncthreads();
+      // digit 3 (key bits 7..0) over the candidates inside bucket b2
+#pragma unroll
+      for (int j = 0; j < kStagePer; ++j)
+        if (cand(j) && (key[j] >> 8) == pre12)
+          atomicAdd(&hist[key[j] & 0xFFu], 1u);
+      __syncthreads();
+      select_bucket<kBins3>(hist, need2, s_scan, s_out);
+      tau = (pre12 << 8) | s_out[0];
+      need_tie = need2 - s_out[1];
+      rank_ties = need_tie < s_out[2];
+    }
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     // entries of this wave before this one (in entry order) that are ties
     uint32_t tie_run = 0;
@@ -538,7 +548,7 @@ __global__ void __launch_bounds__(kThreads) topk_row_kernel(
   __shared__ uint32_t s_ent[kWavesTk][kRowCap];
   __shared__ uint32_t s_key[kWavesTk][kRowCap];
   __shared__ uint32_t s_scan[kThreads + kWavesTk];
-  __shared__ uint32_t s_out[2];
+  __shared__ uint32_t s_out[3];
   __shared__ uint32_t s_cnt[kWavesTk], s_tie[kWavesTk], s_sel[kWavesTk];
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
