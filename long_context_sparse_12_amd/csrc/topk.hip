@@ -674,20 +674,27 @@ __global__ void __launch_bounds__(kThreads) topk_row_kernel(
   select_bucket<kBins2>(hist, need1, s_scan, s_out);
   const uint32_t b2 = s_out[0];
   const uint32_t above2 = s_out[1];
-  __syncthreads();
-  for (int i = tid; i < kBins3; i += kThreads) hist[i] = 0;
-  __syncthreads();
-  const uint32_t pre12 = (b1 << 12) | b2;
-  for (uint32_t e = lane; e < my_n; e += 64) {
-    uint32_t key;
-    const uint32_t v = get(wave, e, key);
-    if (!(v & kSure) && (key >> 8) == pre12) atomicAdd(&hist[key & 0xFFu], 1u);
-  }
-  __syncthreads();
   const uint32_t need2 = need1 - above2;
-  select_bucket<kBins3>(hist, need2, s_scan, s_out);
-  const uint32_t tau = (pre12 << 8) | s_out[0];
-  const uint32_t need_tie = need2 - s_out[1];  // keys equal to tau that are kept
+  const uint32_t pre12 = (b1 << 12) | b2;
+  uint32_t tau, need_tie;  // the smallest kept key; how many keys equal to it are kept
+  if (s_out[2] == need2) {
+    // every candidate of bucket b2 is kept: no third digit
+    tau = pre12 << 8;
+    need_tie = 0xFFFFFFFFu;
+  } else {
+    __syncthreads();
+    for (int i = tid; i < kBins3; i += kThreads) hist[i] = 0;
+    __syncthreads();
+    for (uint32_t e = lane; e < my_n; e += 64) {
+      uint32_t key;
+      const uint32_t v = get(wave, e, key);
+      if (!(v & kSure) && (key >> 8) == pre12) atomicAdd(&hist[key & 0xFFu], 1u);
+    }
+    __syncthreads();
+    select_bucket<kBins3>(hist, need2, s_scan, s_out);
+    tau = (pre12 << 8) | s_out[0];
+    need_tie = need2 - s_out[1];
+  }
 
   // ---- emission in position order (wave order, then list order) ----
   // ties per wave, then each wave's kept count, then the writes
