@@ -386,46 +386,67 @@ def test_indexshare_glm52_schedule_small():
         assert torch.equal(out, layers_d[l]["out"])
 
 
-def test_composite_fused_histogram_matches_separate_calls():
+FUSED_CASES = [
+    # several chunks per row, GLM52 schedule (full layers 0, 1, 2, 6)
+    ("chunks", 4, 20000, 2048, 7, wl.SCHED_GLM52,
+     ([[20000], [13337], [1500], [0]], [[0], [19999], [2048], [20000]])),
+    # one chunk per row (L <= 2048) with rows longer than k
+    ("one-chunk", 3, 2000, 1000, 2, wl.SCHED_GROUP4,
+     ([[2000], [1001], [999]], [[1000], [0], [2000]])),
+    # >= 512 rows of <= 2^18 positions: the one-workgroup-per-row top-k, so
+    # the composite keeps the indexer and the selection separate
+    ("row-kernel", 520, 3000, 2048, 2, wl.SCHED_GROUP4,
+     ([[3000]] * 519 + [[100]], [[2049]] * 520)),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: c[0])
+def test_composite_fused_histogram_matches_separate_calls(case):
     """With one query per sequence the composite call builds the selection's
-    first histogram inside the indexer launch, and each selection leaves it
-    zero for the next full layer (one clear per call). Every full layer's
-    selection must equal separate idx_score + topk_select calls (each checked
-    against the oracle elsewhere) bit for bit, for rows whose visible length is
-    L, ragged, at most k (every position kept) and 0, over two calls that
-    share one workspace."""
-    w = wl.Workload("fused-hist", seed=25, B=4, T=1, L=20000, n_layers=7, sched=wl.SCHED_GLM52,
-                    kv_fp8=True)
-    _say("case: composite fused histogram %s" % w.name)
+    first histogram inside the indexer launch (when the selection takes the
+    chunked launches), and each selection leaves it zero for the next full
+    layer (one clear per call). Every full layer's selection must equal
+    separate idx_score + topk_select calls (each checked against the oracle
+    elsewhere) bit for bit, for rows whose visible length is L, ragged, at
+    most k (every position kept) and 0, over two calls that share one
+    workspace filled with non-zero bytes."""
+    name, B, L, k, n, sched, vis_sets = case
+    w = wl.Workload("fused-" + name, seed=25, B=B, T=1, L=L, n_layers=n, sched=sched,
+                    kv_fp8=True, k=k)
+    _say("case: composite fused histogram %s B=%d L=%d k=%d" % (name, B, L, k))
     full = w.full_layers()
-    assert full == [0, 1, 2, 6]
-    layers_h = _host_layers(w, w.n_layers, full)
-    layers_d = _dev_layers(layers_h)
-    B, T, L, k = w.B, w.T, w.L, w.k
-    for ly in layers_d:
-        ly["out"] = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
-        ly["lse"] = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+    T = 1
+    layers = []
+    for l in range(n):
+        d = wl.dev_indexer(w, l, DEV) if l in full else {}
+        d["q"] = wl.dev_attn_q(w, l, DEV)
+        d["kv"], d["kv_scale"] = wl.dev_kv(w, l, DEV)
+        d["out"] = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+        d["lse"] = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+        layers.append(d)
     idx_out = torch.empty((len(full), B, T, k), dtype=torch.int32, device=DEV)
     scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
     ws = torch.full((lcs.indexshare_workspace_bytes(B, T, L, k),), 0x5A, dtype=torch.uint8,
                     device=DEV)  # not zero: the call clears what it needs
     tk_ws = _zeros(lcs.topk_workspace_bytes(B, T, L, k))
     ref = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
-    for vis in ([[L], [13337], [k - 548], [0]], [[0], [L - 1], [k], [L]]):
+    for vis in vis_sets:
         vis_d = to_dev(np.array(vis, np.int32))
-        lcs.indexshare_forward(layers_d, lcs.SCHED_GLM52, vis_d, k, w.sm_scale, scores, idx_out, ws,
+        lcs.indexshare_forward(layers, sched, vis_d, k, w.sm_scale, scores, idx_out, ws,
                                kv_dtype=lcs.KV_FP8_E4M3)
         torch.cuda.synchronize()
         got = idx_out.cpu().numpy()
         for f, l in enumerate(full):
-            ly = layers_d[l]
+            ly = layers[l]
             lcs.idx_score(ly["q8"], ly["q_scale"], ly["w"], ly["k8"], ly["k_scale"], vis_d, scores)
             lcs.topk_select(scores, vis_d, k, ref, tk_ws)
             torch.cuda.synchronize()
             want = ref.cpu().numpy()
             bad = np.argwhere(got[f] != want)
-            _say("  vis %s full layer %d: %d mismatches" % ([v[0] for v in vis], l, len(bad)))
+            _say("  full layer %d: %d mismatches" % (l, len(bad)))
             assert bad.size == 0, (l, bad[:5])
+    del layers, scores, ws
+    torch.cuda.empty_cache()
 
 
 def test_composite_decode128k_full_size_sampled():
