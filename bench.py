@@ -36,8 +36,8 @@ ROTATIONS = 3  # query sets cycled between steps so no step reuses another's gat
 # scaled by the copy-kernel calibration; valid only for the kernel source it was
 # taken on (sha256 of csrc/idx_score.hip, first 16 hex digits).
 TRAFFIC = {
-    "decode-B32-L131072-group4": {"sha": "e548809405f0e7c3", "bytes": 572196150},
-    "decode-B2-L1048576-78layers-fp8kv": {"sha": "e548809405f0e7c3", "bytes": 285377915},
+    "decode-B32-L131072-group4": {"sha": "6bfa7e3d3b42758a", "bytes": 572135072},
+    "decode-B2-L1048576-78layers-fp8kv": {"sha": "6bfa7e3d3b42758a", "bytes": 285334803},
 }
 
 

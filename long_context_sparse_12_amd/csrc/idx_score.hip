@@ -19,7 +19,7 @@ namespace lcs {
 namespace {
 
 #ifndef LCS_IDX_TARGET_WGS
-#define LCS_IDX_TARGET_WGS 1024
+#define LCS_IDX_TARGET_WGS 512
 #endif
 #ifndef LCS_IDX_PREFILL_MIN_T
 #define LCS_IDX_PREFILL_MIN_T 16
