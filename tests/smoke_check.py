@@ -1,6 +1,7 @@
-"""One small decode pass of the whole path on cuda:0, checked against the oracle:
-the tiny IndexShare group (1 x 4 queries, L = 8192, layer 0 full, layers 1-3
-reuse its top-2048)."""
+"""Small passes of the whole path on cuda:0, checked against the oracle: the
+tiny IndexShare group (1 x 4 queries, L = 8192, layer 0 full, layers 1-3 reuse
+its top-2048), and a decode group with one query per sequence (4 x 1, L =
+8192), whose indexer launch also builds the top-k histogram."""
 import numpy as np
 import torch
 
@@ -10,8 +11,7 @@ from synth import workloads as wl
 from tests.parity import DEV, check_attention, check_selection, to_dev
 
 
-def run_smoke():
-    w = wl.WORKLOADS["tiny"]
+def _one(w):
     B, T, L, k = w.B, w.T, w.L, w.k
     vis = w.vis_len()
     layers_h = []
@@ -46,3 +46,9 @@ def run_smoke():
             worst = max(worst, mx)
     print("smoke ok: %s, selection overlap %.5f (worst gap %.2g), attention max-abs %.3g"
           % (w.name, overlap, gap, worst), flush=True)
+
+
+def run_smoke():
+    _one(wl.WORKLOADS["tiny"])
+    _one(wl.Workload("decode-smoke", seed=6, B=4, T=1, L=8192, n_layers=4,
+                     plant_permyriad=100))
