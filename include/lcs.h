@@ -18,8 +18,14 @@
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers owned by the caller, contiguous,
- *    row-major in the order given, and 16-byte aligned. bf16 values are passed
- *    as uint16_t bit patterns. FP8 values are OCP E4M3 codes (bias 7, max 448).
+ *    row-major in the order given, and 16-byte aligned; the key and latent
+ *    caches of lcs_idx_score and lcs_sparse_mla_attn may instead place the
+ *    sequences a batch stride apart (a view of a larger cache). bf16 values are
+ *    passed as uint16_t bit patterns. FP8 values are OCP E4M3 codes (bias 7,
+ *    max 448).
+ *  - Outputs (and workspaces) must not overlap any other buffer of the call;
+ *    inputs may share memory. A call whose byte ranges break this returns
+ *    LCS_ERR_SHAPE naming the two buffers.
  *  - Calls are asynchronous on `stream` (NULL = the default stream). The
  *    library never allocates, frees or synchronises, and keeps no state
  *    between calls except inside caller-provided workspaces.
@@ -49,7 +55,8 @@ typedef struct ihipStream_t* hipStream_t;
 typedef enum {
   LCS_OK = 0,
   LCS_ERR_NULL = 1,        /* a required pointer is NULL */
-  LCS_ERR_SHAPE = 2,       /* a size is out of range, or a pointer misaligned */
+  LCS_ERR_SHAPE = 2,       /* a size is out of range, a pointer misaligned, or an output
+                              overlaps another buffer */
   LCS_ERR_UNSUPPORTED = 3, /* k outside [1, 2048], an unknown enum value */
   LCS_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
   LCS_ERR_HIP = 5          /* a HIP launch or runtime call failed */
@@ -71,8 +78,12 @@ typedef enum { LCS_KV_BF16 = 0, LCS_KV_FP8_E4M3 = 1 } lcs_kv_dtype;
  * q8      [B][T][32][128] E4M3 query codes
  * q_scale [B][T][32]      fp32 dequantisation scale per (query, head), > 0
  * w       [B][T][32]      fp32 head weights
- * k8      [B][L][128]     E4M3 key codes;  k_scale [B][L] fp32 per-key scale
- * vis_len [B][T]          int32 visible prefix length of each query
+ * k8      [B][L][128]     E4M3 key codes;  k_scale [B][L] fp32 per-key scale;
+ *                         sequence b's rows start at row b * k_batch_stride of
+ *                         both (k_batch_stride >= L; L for a dense cache), so
+ *                         a cache of more positions can be scored on its
+ *                         first L
+ * vis_len [B][T]          int32 visible prefix length of each query (L < 2^30)
  * scores  [B][T][L]       fp32 output:
  *   scores[b,t,s] = k_scale[s] * sum_j w[j]*q_scale[j] * relu(q8[j] . k8[s])
  *   for s < vis_len[b,t], -inf otherwise.
@@ -80,7 +91,7 @@ typedef enum { LCS_KV_BF16 = 0, LCS_KV_FP8_E4M3 = 1 } lcs_kv_dtype;
  * up to 6 queries, the 32 heads as the FP8 MFMA M dimension); T >= 16 uses a
  * tiled FP8 MFMA kernel. */
 lcs_status lcs_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
-                         const uint8_t* k8, const float* k_scale,
+                         const uint8_t* k8, const float* k_scale, int64_t k_batch_stride,
                          const int32_t* vis_len, int32_t B, int32_t T, int32_t L,
                          float* scores, hipStream_t stream);
 
@@ -104,7 +115,9 @@ size_t lcs_attn_workspace_bytes(int32_t B, int32_t T, int32_t k);
 /* Sparse MLA attention over the selected rows, absorbed form.
  * q   [B][T][64][576] bf16
  * kv  [B][L][576] bf16 (LCS_KV_BF16), or E4M3 codes with kv_scale [B][L]
- *     fp32 (LCS_KV_FP8_E4M3; kv_scale must be NULL for bf16)
+ *     fp32 (LCS_KV_FP8_E4M3; kv_scale must be NULL for bf16); sequence b's
+ *     rows start at row b * kv_batch_stride of both (kv_batch_stride >= L; L
+ *     for a dense cache)
  * idx [B][T][k] int32 positions in [0, L), or -1 for an empty slot
  * out [B][T][64][512] bf16 = softmax_i(sm_scale * q . kv[idx_i]) . kv[idx_i][0:512]
  * lse [B][T][64] fp32 natural-log sum of exp of the scaled logits (nullable);
@@ -112,7 +125,8 @@ size_t lcs_attn_workspace_bytes(int32_t B, int32_t T, int32_t k);
  * Positions outside [-1, L) are a caller error (not checked on the device). */
 lcs_status lcs_sparse_mla_attn(const uint16_t* q, const void* kv,
                                lcs_kv_dtype kv_dtype, const float* kv_scale,
-                               const int32_t* idx, int32_t B, int32_t T, int32_t L,
+                               int64_t kv_batch_stride, const int32_t* idx, int32_t B,
+                               int32_t T, int32_t L,
                                int32_t k, float sm_scale, uint16_t* out, float* lse,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream);

@@ -66,12 +66,13 @@ def _sig(name, res, args):
     return f
 
 
-_c_idx_score = _sig("lcs_idx_score", ctypes.c_int, [_p] * 6 + [_i32] * 3 + [_p, _p])
+_i64 = ctypes.c_int64
+_c_idx_score = _sig("lcs_idx_score", ctypes.c_int, [_p] * 5 + [_i64, _p] + [_i32] * 3 + [_p, _p])
 _c_topk_ws = _sig("lcs_topk_workspace_bytes", _sz, [_i32] * 4)
 _c_topk = _sig("lcs_topk_select", ctypes.c_int, [_p, _p] + [_i32] * 4 + [_p, _p, _sz, _p])
 _c_attn_ws = _sig("lcs_attn_workspace_bytes", _sz, [_i32] * 3)
 _c_attn = _sig("lcs_sparse_mla_attn", ctypes.c_int,
-               [_p, _p, ctypes.c_int, _p, _p] + [_i32] * 4 + [_f32, _p, _p, _p, _sz, _p])
+               [_p, _p, ctypes.c_int, _p, _i64, _p] + [_i32] * 4 + [_f32, _p, _p, _p, _sz, _p])
 _c_count = _sig("lcs_count_full_layers", _i32, [ctypes.c_int, _i32, _p, _i32])
 _c_is_ws = _sig("lcs_indexshare_workspace_bytes", _sz, [_i32] * 4)
 _c_is = _sig("lcs_indexshare_forward", ctypes.c_int,
@@ -108,6 +109,23 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _batch_stride(cache, row_width, scale=None):
+    """Rows from one sequence of a [B, L, row_width] cache view to the next (its rows
+    themselves dense), checked against the view of its per-row scales [B, L]"""
+    if cache.dim() != 3 or cache.shape[2] != row_width or cache.stride(2) != 1 or \
+            (cache.shape[1] > 1 and cache.stride(1) != row_width) or cache.stride(0) % row_width:
+        raise ValueError("cache must be a [B, L, %d] view with dense rows" % row_width)
+    stride = cache.stride(0) // row_width
+    if cache.shape[0] == 1:
+        stride = cache.shape[1]
+    if scale is not None and scale.shape[0] > 1 and \
+            (scale.stride(1) != 1 or scale.stride(0) != stride):
+        raise ValueError("scales must have the cache's batch stride (%d rows)" % stride)
+    if scale is not None and scale.stride(-1) != 1:
+        raise ValueError("scales must be dense along L")
+    return stride
+
+
 def _stream(stream):
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -117,11 +135,13 @@ def _stream(stream):
 
 def idx_score(q8, q_scale, w, k8, k_scale, vis_len, scores, stream=None):
     """scores[B,T,L] (fp32) from q8[B,T,32,128], q_scale/w[B,T,32], k8[B,L,128],
-    k_scale[B,L], vis_len[B,T] (int32)."""
+    k_scale[B,L], vis_len[B,T] (int32). k8/k_scale may be views of a longer cache
+    (k8[:, :L]): their batch stride is passed on."""
     B, T = q8.shape[0], q8.shape[1]
     L = k8.shape[1]
     _check(_c_idx_score(_ptr(q8), _ptr(q_scale), _ptr(w), _ptr(k8), _ptr(k_scale),
-                        _ptr(vis_len), B, T, L, _ptr(scores), _stream(stream)))
+                        _batch_stride(k8, IDX_DIM, k_scale), _ptr(vis_len), B, T, L,
+                        _ptr(scores), _stream(stream)))
 
 
 def topk_workspace_bytes(B, T, L, k):
@@ -150,11 +170,12 @@ def _kv_dtype(kv):
 
 def sparse_mla_attn(q, kv, kv_scale, idx, sm_scale, out, lse=None, workspace=None, stream=None):
     """out[B,T,64,512] (bf16) from q[B,T,64,576] (bf16), kv[B,L,576] (bf16, or uint8 E4M3
-    codes with kv_scale[B,L]), idx[B,T,k]."""
+    codes with kv_scale[B,L]), idx[B,T,k]. kv/kv_scale may be views of a longer cache."""
     B, T = q.shape[0], q.shape[1]
     L = kv.shape[1]
     k = idx.shape[-1]
-    _check(_c_attn(_ptr(q), _ptr(kv), _kv_dtype(kv), _ptr(kv_scale), _ptr(idx), B, T, L, k,
+    _check(_c_attn(_ptr(q), _ptr(kv), _kv_dtype(kv), _ptr(kv_scale),
+                   _batch_stride(kv, KV_DIM, kv_scale), _ptr(idx), B, T, L, k,
                    float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                    0 if workspace is None else workspace.numel() * workspace.element_size(),
                    _stream(stream)))

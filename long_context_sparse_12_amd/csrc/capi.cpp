@@ -7,6 +7,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "../../include/lcs.h"
 #include "common.h"
 
@@ -29,12 +32,14 @@ lcs_status ok() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-constexpr int32_t kMaxL = 1 << 30;
+// L < 2^30: a score row of L fp32 values then spans fewer than 2^32 bytes, the
+// range a 32-bit buffer descriptor (and its unsigned byte offsets) covers.
+constexpr int32_t kMaxL = (1 << 30) - 1;
 
 lcs_status check_dims(int32_t B, int32_t T, int32_t L) {
   if (B <= 0 || T <= 0 || L <= 0)
     return fail(LCS_ERR_SHAPE, "B, T and L must be positive (got %d, %d, %d)", B, T, L);
-  if (L > kMaxL) return fail(LCS_ERR_SHAPE, "L = %d exceeds 2^30", L);
+  if (L > kMaxL) return fail(LCS_ERR_SHAPE, "L = %d is not below 2^30", L);
   if ((int64_t)B * T > (1LL << 31) - 1) return fail(LCS_ERR_SHAPE, "B*T too large");
   if ((int64_t)B * L > (1LL << 40)) return fail(LCS_ERR_SHAPE, "B*L too large");
   return LCS_OK;
@@ -63,9 +68,103 @@ lcs_status hip_status(hipError_t e, const char* what) {
   return LCS_OK;
 }
 
+// Rows (tokens) from one sequence's cache rows to the next: at least L, and
+// the rows the B sequences span stay within 2^40.
+lcs_status check_stride(int64_t stride, int32_t B, int32_t L, const char* name) {
+  if (stride < L)
+    return fail(LCS_ERR_SHAPE, "%s = %lld is below L = %d", name, (long long)stride, L);
+  if (stride > (1LL << 40) || (int64_t)(B - 1) * stride + L > (1LL << 40))
+    return fail(LCS_ERR_SHAPE, "%s = %lld: the cache would span more than 2^40 rows", name,
+                (long long)stride);
+  return LCS_OK;
+}
+
+// Byte ranges of a call's buffers. Inputs may share memory with one another;
+// an output (or a workspace) that overlaps any other buffer is rejected, since
+// the kernels read inputs while they write outputs.
+class Regions {
+ public:
+  void in(const void* p, size_t bytes, const char* name, int layer = -1) {
+    add(p, bytes, name, layer, false);
+  }
+  void out(const void* p, size_t bytes, const char* name, int layer = -1) {
+    add(p, bytes, name, layer, true);
+  }
+  lcs_status check() {
+    std::sort(r_.begin(), r_.end(), [](const R& a, const R& b) {
+      return a.lo != b.lo ? a.lo < b.lo : a.out > b.out;
+    });
+    const R* any = nullptr;  // the earlier range reaching furthest
+    const R* out = nullptr;  // ... among the outputs
+    for (const R& x : r_) {
+      const R* hit = x.out ? any : out;
+      if (hit && x.lo < hit->hi) {
+        char a[64], b[64];
+        return fail(LCS_ERR_SHAPE, "%s overlaps %s (outputs must not alias other buffers)",
+                    label(x, a), label(*hit, b));
+      }
+      if (!any || x.hi > any->hi) any = &x;
+      if (x.out && (!out || x.hi > out->hi)) out = &x;
+    }
+    return LCS_OK;
+  }
+
+ private:
+  struct R {
+    uintptr_t lo, hi;
+    const char* name;
+    int layer;
+    bool out;
+  };
+  static const char* label(const R& x, char (&buf)[64]) {
+    if (x.layer < 0) return x.name;
+    snprintf(buf, sizeof(buf), "layer %d %s", x.layer, x.name);
+    return buf;
+  }
+  void add(const void* p, size_t bytes, const char* name, int layer, bool is_out) {
+    if (!p || bytes == 0) return;
+    const uintptr_t lo = (uintptr_t)p;
+    r_.push_back(R{lo, lo + bytes, name, layer, is_out});
+  }
+  std::vector<R> r_;
+};
+
+constexpr size_t kQ8Bytes = (size_t)LCS_IDX_HEADS * LCS_IDX_DIM;    // per query
+constexpr size_t kQBytes = (size_t)LCS_ATT_HEADS * LCS_KV_DIM * 2;  // per query
+constexpr size_t kOutBytes = (size_t)LCS_ATT_HEADS * LCS_KV_LATENT * 2;
+
+// rows spanned by B sequences of L rows, `stride` rows apart
+size_t span_rows(int32_t B, int32_t L, int64_t stride) {
+  return (size_t)((int64_t)(B - 1) * stride + L);
+}
+
+void indexer_regions(Regions& g, const uint8_t* q8, const float* q_scale, const float* w,
+                     const uint8_t* k8, const float* k_scale, int64_t kstride,
+                     const int32_t* vis_len, int32_t B, int32_t T, int32_t L, int layer = -1) {
+  const size_t q = (size_t)B * T;
+  g.in(q8, q * kQ8Bytes, "q8", layer);
+  g.in(q_scale, q * LCS_IDX_HEADS * 4, "q_scale", layer);
+  g.in(w, q * LCS_IDX_HEADS * 4, "w", layer);
+  g.in(k8, span_rows(B, L, kstride) * LCS_IDX_DIM, "k8", layer);
+  g.in(k_scale, span_rows(B, L, kstride) * 4, "k_scale", layer);
+  g.in(vis_len, q * 4, "vis_len");
+}
+
+void attn_regions(Regions& g, const uint16_t* q, const void* kv, bool fp8, const float* kv_scale,
+                  int64_t kv_stride, int32_t B, int32_t T, int32_t L, const uint16_t* out,
+                  const float* lse, int layer = -1) {
+  const size_t nq = (size_t)B * T;
+  g.in(q, nq * kQBytes, "q", layer);
+  g.in(kv, span_rows(B, L, kv_stride) * (fp8 ? LCS_KV_DIM : 2 * LCS_KV_DIM), "kv", layer);
+  g.in(kv_scale, span_rows(B, L, kv_stride) * 4, "kv_scale", layer);
+  g.out(out, nq * kOutBytes, "out", layer);
+  g.out(lse, nq * LCS_ATT_HEADS * 4, "lse", layer);
+}
+
 lcs_status validate_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
-                              const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
-                              int32_t B, int32_t T, int32_t L, const float* scores) {
+                              const uint8_t* k8, const float* k_scale, int64_t kstride,
+                              const int32_t* vis_len, int32_t B, int32_t T, int32_t L,
+                              const float* scores) {
   REQUIRE(q8, "q8");
   REQUIRE(q_scale, "q_scale");
   REQUIRE(w, "w");
@@ -74,6 +173,7 @@ lcs_status validate_idx_score(const uint8_t* q8, const float* q_scale, const flo
   REQUIRE(vis_len, "vis_len");
   REQUIRE(scores, "scores");
   TRY(check_dims(B, T, L));
+  TRY(check_stride(kstride, B, L, "k_batch_stride"));
   return LCS_OK;
 }
 
@@ -94,9 +194,9 @@ lcs_status validate_topk(const float* scores, const int32_t* vis_len, int32_t B,
 }
 
 lcs_status validate_attn(const uint16_t* q, const void* kv, int kv_dtype, const float* kv_scale,
-                         const int32_t* idx, int32_t B, int32_t T, int32_t L, int32_t k,
-                         float sm_scale, const uint16_t* out, const float* lse, const void* ws,
-                         size_t ws_bytes) {
+                         int64_t kv_stride, const int32_t* idx, int32_t B, int32_t T, int32_t L,
+                         int32_t k, float sm_scale, const uint16_t* out, const float* lse,
+                         const void* ws, size_t ws_bytes) {
   REQUIRE(q, "q");
   REQUIRE(kv, "kv");
   REQUIRE(idx, "idx");
@@ -110,6 +210,7 @@ lcs_status validate_attn(const uint16_t* q, const void* kv, int kv_dtype, const 
     return fail(LCS_ERR_SHAPE, "kv_scale must be NULL for bf16 kv");
   }
   TRY(check_dims(B, T, L));
+  TRY(check_stride(kv_stride, B, L, "kv_batch_stride"));
   TRY(check_k(k));
   if (!(sm_scale > 0.f) || sm_scale != sm_scale || sm_scale > 1e30f)
     return fail(LCS_ERR_SHAPE, "sm_scale must be a finite positive number");
@@ -151,6 +252,27 @@ lcs_status validate_append(const uint16_t* k_new, const uint16_t* kv_new, int kv
   }
   TRY(check_dims(B, T, L));
   return LCS_OK;
+}
+
+// The new rows and positions are read while the caches are written.
+lcs_status check_append_regions(const uint16_t* k_new, const uint16_t* kv_new, int kv_dtype,
+                                const int32_t* pos, int32_t B, int32_t T, const void* k8,
+                                size_t k8_bytes, const void* k_scale, size_t ks_bytes,
+                                const void* kv, size_t kv_bytes, const void* kv_scale,
+                                size_t kvs_bytes, const int32_t* table = nullptr,
+                                size_t table_bytes = 0) {
+  (void)kv_dtype;
+  const size_t nt = (size_t)B * T;
+  Regions g;
+  g.in(k_new, nt * LCS_IDX_DIM * 2, "k_new");
+  g.in(kv_new, nt * LCS_KV_DIM * 2, "kv_new");
+  g.in(pos, nt * 4, "pos");
+  g.in(table, table_bytes, "block_table");
+  g.out(k8, k8_bytes, "k8");
+  g.out(k_scale, ks_bytes, "k_scale");
+  g.out(kv, kv_bytes, "kv");
+  g.out(kv_scale, kvs_bytes, "kv_scale");
+  return g.check();
 }
 
 // A paged layout: a table of int32 pool blocks, power-of-two blocks of at
@@ -209,11 +331,16 @@ const char* lcs_status_string(lcs_status s) {
 const char* lcs_last_error(void) { return g_err; }
 
 lcs_status lcs_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
-                         const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
-                         int32_t B, int32_t T, int32_t L, float* scores, hipStream_t stream) {
-  TRY(validate_idx_score(q8, q_scale, w, k8, k_scale, vis_len, B, T, L, scores));
-  TRY(hip_status(lcs::launch_idx_score(q8, q_scale, w, k8, k_scale, vis_len, B, T, L, scores,
-                                       stream),
+                         const uint8_t* k8, const float* k_scale, int64_t k_batch_stride,
+                         const int32_t* vis_len, int32_t B, int32_t T, int32_t L, float* scores,
+                         hipStream_t stream) {
+  TRY(validate_idx_score(q8, q_scale, w, k8, k_scale, k_batch_stride, vis_len, B, T, L, scores));
+  Regions g;
+  indexer_regions(g, q8, q_scale, w, k8, k_scale, k_batch_stride, vis_len, B, T, L);
+  g.out(scores, (size_t)B * T * L * 4, "scores");
+  TRY(g.check());
+  TRY(hip_status(lcs::launch_idx_score(q8, q_scale, w, k8, k_scale, k_batch_stride, vis_len, B, T,
+                                       L, scores, stream),
                  "idx_score launch"));
   return ok();
 }
@@ -227,6 +354,12 @@ lcs_status lcs_topk_select(const float* scores, const int32_t* vis_len, int32_t 
                            int32_t L, int32_t k, int32_t* idx, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
   TRY(validate_topk(scores, vis_len, B, T, L, k, idx, workspace, workspace_bytes));
+  Regions g;
+  g.in(scores, (size_t)B * T * L * 4, "scores");
+  g.in(vis_len, (size_t)B * T * 4, "vis_len");
+  g.out(idx, (size_t)B * T * k * 4, "idx");
+  g.out(workspace, lcs::topk_workspace_bytes((int64_t)B * T, L, k), "workspace");
+  TRY(g.check());
   TRY(hip_status(lcs::launch_topk(scores, vis_len, B * T, L, k, idx, workspace, stream),
                  "topk launch"));
   return ok();
@@ -238,13 +371,21 @@ size_t lcs_attn_workspace_bytes(int32_t B, int32_t T, int32_t k) {
 }
 
 lcs_status lcs_sparse_mla_attn(const uint16_t* q, const void* kv, lcs_kv_dtype kv_dtype,
-                               const float* kv_scale, const int32_t* idx, int32_t B, int32_t T,
-                               int32_t L, int32_t k, float sm_scale, uint16_t* out, float* lse,
-                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  TRY(validate_attn(q, kv, (int)kv_dtype, kv_scale, idx, B, T, L, k, sm_scale, out, lse,
-                    workspace, workspace_bytes));
-  TRY(hip_status(lcs::launch_sparse_mla(q, kv, kv_dtype == LCS_KV_FP8_E4M3, kv_scale, idx, B, T,
-                                        L, k, sm_scale, out, lse, workspace, stream),
+                               const float* kv_scale, int64_t kv_batch_stride, const int32_t* idx,
+                               int32_t B, int32_t T, int32_t L, int32_t k, float sm_scale,
+                               uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  TRY(validate_attn(q, kv, (int)kv_dtype, kv_scale, kv_batch_stride, idx, B, T, L, k, sm_scale,
+                    out, lse, workspace, workspace_bytes));
+  Regions g;
+  attn_regions(g, q, kv, kv_dtype == LCS_KV_FP8_E4M3, kv_scale, kv_batch_stride, B, T, L, out,
+               lse);
+  g.in(idx, (size_t)B * T * k * 4, "idx");
+  g.out(workspace, lcs::attn_workspace_bytes((int64_t)B * T, k), "workspace");
+  TRY(g.check());
+  TRY(hip_status(lcs::launch_sparse_mla(q, kv, kv_dtype == LCS_KV_FP8_E4M3, kv_scale,
+                                        kv_batch_stride, idx, B, T, L, k, sm_scale, out, lse,
+                                        workspace, stream),
                  "sparse_mla launch"));
   return ok();
 }
@@ -259,6 +400,11 @@ lcs_status lcs_quantize_e4m3(const uint16_t* x, int64_t rows, int32_t D, uint8_t
   REQUIRE(x, "x");
   REQUIRE(codes, "codes");
   REQUIRE(scales, "scales");
+  Regions g;
+  g.in(x, (size_t)rows * D * 2, "x");
+  g.out(codes, (size_t)rows * D, "codes");
+  g.out(scales, (size_t)rows * 4, "scales");
+  TRY(g.check());
   TRY(hip_status(lcs::launch_quantize_e4m3(x, rows, D, codes, scales, stream),
                  "quantize launch"));
   return ok();
@@ -268,6 +414,11 @@ lcs_status lcs_cache_append(const uint16_t* k_new, const uint16_t* kv_new, lcs_k
                             const int32_t* pos, int32_t B, int32_t T, int32_t L, uint8_t* k8,
                             float* k_scale, void* kv, float* kv_scale, hipStream_t stream) {
   TRY(validate_append(k_new, kv_new, (int)kv_dtype, pos, B, T, L, k8, k_scale, kv, kv_scale));
+  const size_t rows = (size_t)B * L;
+  TRY(check_append_regions(k_new, kv_new, kv_dtype, pos, B, T, k8, rows * LCS_IDX_DIM, k_scale,
+                           rows * 4, kv,
+                           rows * (kv_dtype == LCS_KV_FP8_E4M3 ? LCS_KV_DIM : 2 * LCS_KV_DIM),
+                           kv_scale, rows * 4));
   TRY(hip_status(lcs::launch_cache_append(k_new, kv_new, kv_dtype == LCS_KV_FP8_E4M3, pos, B, T,
                                           L, k8, k_scale, kv, kv_scale, nullptr, 0, 0, 0, stream),
                  "cache_append launch"));
@@ -286,6 +437,14 @@ lcs_status lcs_topk_candidates(const float* scores, const int32_t* idx, int32_t 
   if (pos_base < 0 || (int64_t)pos_base + L > 0x7FFFFFFF)
     return fail(LCS_ERR_SHAPE, "pos_base = %d: positions pos_base + [0, L) must fit in int32",
                 pos_base);
+  {
+    Regions g;
+    g.in(scores, (size_t)B * T * L * 4, "scores");
+    g.in(idx, (size_t)B * T * k * 4, "idx");
+    g.out(cand_score, (size_t)B * T * k * 4, "cand_score");
+    g.out(cand_idx, (size_t)B * T * k * 4, "cand_idx");
+    TRY(g.check());
+  }
   TRY(hip_status(lcs::launch_topk_candidates(scores, idx, (int64_t)B * T, L, k, pos_base,
                                              cand_score, cand_idx, stream),
                  "topk_candidates launch"));
@@ -303,6 +462,13 @@ lcs_status lcs_topk_merge(const float* cand_score, const int32_t* cand_idx, int3
                 (long long)G * k_in, LCS_MAX_MERGE_CANDIDATES);
   TRY(check_dims(B, T, 1));
   TRY(check_k(k));
+  {
+    Regions g;
+    g.in(cand_score, (size_t)G * k_in * B * T * 4, "cand_score");
+    g.in(cand_idx, (size_t)G * k_in * B * T * 4, "cand_idx");
+    g.out(idx, (size_t)B * T * k * 4, "idx");
+    TRY(g.check());
+  }
   TRY(hip_status(lcs::launch_topk_merge(cand_score, cand_idx, G, (int64_t)B * T, k_in, k, idx,
                                         stream),
                  "topk_merge launch"));
@@ -313,9 +479,14 @@ lcs_status lcs_idx_localize(const int32_t* idx, int32_t B, int32_t T, int32_t k,
                             int32_t hi, int32_t* local, hipStream_t stream) {
   REQUIRE(idx, "idx");
   REQUIRE(local, "local");
-  if (idx == local) return fail(LCS_ERR_SHAPE, "idx and local must not alias");
   TRY(check_dims(B, T, 1));
   TRY(check_k(k));
+  {
+    Regions g;
+    g.in(idx, (size_t)B * T * k * 4, "idx");
+    g.out(local, (size_t)B * T * k * 4, "local");
+    TRY(g.check());
+  }
   if (lo < 0 || hi < lo) return fail(LCS_ERR_SHAPE, "need 0 <= lo <= hi (got %d, %d)", lo, hi);
   TRY(hip_status(lcs::launch_idx_localize(idx, (int64_t)B * T, k, lo, hi, local, stream),
                  "idx_localize launch"));
@@ -331,6 +502,15 @@ lcs_status lcs_lse_combine(const uint16_t* part_out, const float* part_lse, int3
   if (G <= 0 || G > LCS_MAX_SHARDS)
     return fail(LCS_ERR_SHAPE, "G = %d outside [1, %d]", G, LCS_MAX_SHARDS);
   TRY(check_dims(B, T, 1));
+  {
+    const size_t nq = (size_t)B * T;
+    Regions g;
+    g.in(part_out, (size_t)G * nq * kOutBytes, "part_out");
+    g.in(part_lse, (size_t)G * nq * LCS_ATT_HEADS * 4, "part_lse");
+    g.out(out, nq * kOutBytes, "out");
+    g.out(lse, nq * LCS_ATT_HEADS * 4, "lse");
+    TRY(g.check());
+  }
   TRY(hip_status(lcs::launch_lse_combine(part_out, part_lse, G, (int64_t)B * T, out, lse, stream),
                  "lse_combine launch"));
   return ok();
@@ -340,9 +520,19 @@ lcs_status lcs_idx_score_paged(const uint8_t* q8, const float* q_scale, const fl
                                const uint8_t* k8_pool, const float* k_scale_pool,
                                const lcs_paged* paged, const int32_t* vis_len, int32_t B,
                                int32_t T, int32_t L, float* scores, hipStream_t stream) {
-  TRY(validate_idx_score(q8, q_scale, w, k8_pool, k_scale_pool, vis_len, B, T, L, scores));
+  TRY(validate_idx_score(q8, q_scale, w, k8_pool, k_scale_pool, L, vis_len, B, T, L, scores));
   int lbs = 0;
   TRY(validate_paged(paged, L, &lbs));
+  {
+    const size_t pool_rows = (size_t)paged->n_blocks * paged->block_size;
+    Regions g;
+    indexer_regions(g, q8, q_scale, w, nullptr, nullptr, L, vis_len, B, T, L);
+    g.in(k8_pool, pool_rows * LCS_IDX_DIM, "k8_pool");
+    g.in(k_scale_pool, pool_rows * 4, "k_scale_pool");
+    g.in(paged->block_table, (size_t)B * paged->max_blocks * 4, "block_table");
+    g.out(scores, (size_t)B * T * L * 4, "scores");
+    TRY(g.check());
+  }
   TRY(hip_status(lcs::launch_idx_score_paged(q8, q_scale, w, k8_pool, k_scale_pool,
                                              paged->block_table, paged->max_blocks, lbs,
                                              paged->n_blocks, vis_len, B, T, L, scores, stream),
@@ -356,10 +546,22 @@ lcs_status lcs_sparse_mla_attn_paged(const uint16_t* q, const void* kv_pool,
                                      int32_t T, int32_t L, int32_t k, float sm_scale,
                                      uint16_t* out, float* lse, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream) {
-  TRY(validate_attn(q, kv_pool, (int)kv_dtype, kv_scale_pool, idx, B, T, L, k, sm_scale, out, lse,
-                    workspace, workspace_bytes));
+  TRY(validate_attn(q, kv_pool, (int)kv_dtype, kv_scale_pool, L, idx, B, T, L, k, sm_scale, out,
+                    lse, workspace, workspace_bytes));
   int lbs = 0;
   TRY(validate_paged(paged, L, &lbs));
+  {
+    const size_t pool_rows = (size_t)paged->n_blocks * paged->block_size;
+    Regions g;
+    attn_regions(g, q, nullptr, false, nullptr, L, B, T, L, out, lse);
+    g.in(kv_pool, pool_rows * (kv_dtype == LCS_KV_FP8_E4M3 ? LCS_KV_DIM : 2 * LCS_KV_DIM),
+         "kv_pool");
+    g.in(kv_scale_pool, pool_rows * 4, "kv_scale_pool");
+    g.in(paged->block_table, (size_t)B * paged->max_blocks * 4, "block_table");
+    g.in(idx, (size_t)B * T * k * 4, "idx");
+    g.out(workspace, lcs::attn_workspace_bytes((int64_t)B * T, k), "workspace");
+    TRY(g.check());
+  }
   TRY(hip_status(lcs::launch_sparse_mla_paged(q, kv_pool, kv_dtype == LCS_KV_FP8_E4M3,
                                               kv_scale_pool, paged->block_table,
                                               paged->max_blocks, lbs, paged->n_blocks, idx, B, T,
@@ -377,6 +579,13 @@ lcs_status lcs_cache_append_paged(const uint16_t* k_new, const uint16_t* kv_new,
                       kv_scale_pool));
   int lbs = 0;
   TRY(validate_paged(paged, L, &lbs));
+  {
+    const size_t rows = (size_t)paged->n_blocks * paged->block_size;
+    TRY(check_append_regions(
+        k_new, kv_new, kv_dtype, pos, B, T, k8_pool, rows * LCS_IDX_DIM, k_scale_pool, rows * 4,
+        kv_pool, rows * (kv_dtype == LCS_KV_FP8_E4M3 ? LCS_KV_DIM : 2 * LCS_KV_DIM),
+        kv_scale_pool, rows * 4, paged->block_table, (size_t)B * paged->max_blocks * 4));
+  }
   TRY(hip_status(lcs::launch_cache_append(k_new, kv_new, kv_dtype == LCS_KV_FP8_E4M3, pos, B, T, L,
                                           k8_pool, k_scale_pool, kv_pool, kv_scale_pool,
                                           paged->block_table, paged->max_blocks, lbs,
@@ -435,20 +644,37 @@ lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers, lcs
   const size_t ws_attn_bytes = lcs::attn_workspace_bytes((int64_t)B * T, k);
 
   // validate every layer before launching anything
+  const bool fp8 = kv_dtype == LCS_KV_FP8_E4M3;
+  Regions g;
+  int32_t n_full = 0;
   for (int32_t l = 0; l < n_layers; ++l) {
     const lcs_layer& ly = layers[l];
     const bool full = mtp_steps > 0 ? l == 0 : is_full_layer(sched, l, full_mask);
     const lcs_layer& kvl = mtp_steps > 0 ? layers[0] : ly;
     lcs_status s;
+    char cause[sizeof(g_err)];
     if (full) {
-      s = validate_idx_score(ly.q8, ly.q_scale, ly.w, ly.k8, ly.k_scale, vis_len, B, T, L,
+      ++n_full;
+      s = validate_idx_score(ly.q8, ly.q_scale, ly.w, ly.k8, ly.k_scale, L, vis_len, B, T, L,
                              scores_scratch);
-      if (s != LCS_OK) return fail(s, "layer %d indexer: %s", l, g_err);
+      if (s != LCS_OK) {
+        memcpy(cause, g_err, sizeof(cause));  // the message below is formatted into g_err
+        return fail(s, "layer %d indexer: %s", l, cause);
+      }
+      indexer_regions(g, ly.q8, ly.q_scale, ly.w, ly.k8, ly.k_scale, L, vis_len, B, T, L, l);
     }
-    s = validate_attn(ly.q, kvl.kv, (int)kv_dtype, kvl.kv_scale, idx_out, B, T, L, k, sm_scale,
+    s = validate_attn(ly.q, kvl.kv, (int)kv_dtype, kvl.kv_scale, L, idx_out, B, T, L, k, sm_scale,
                       ly.out, ly.lse, ws_attn, ws_attn_bytes);
-    if (s != LCS_OK) return fail(s, "layer %d attention: %s", l, g_err);
+    if (s != LCS_OK) {
+      memcpy(cause, g_err, sizeof(cause));
+      return fail(s, "layer %d attention: %s", l, cause);
+    }
+    attn_regions(g, ly.q, kvl.kv, fp8, kvl.kv_scale, L, B, T, L, ly.out, ly.lse, l);
   }
+  g.out(scores_scratch, (size_t)B * T * L * 4, "scores_scratch");
+  g.out(idx_out, (size_t)n_full * B * T * k * 4, "idx_out");
+  g.out(workspace, need, "workspace");
+  TRY(g.check());
 
   const size_t per = (size_t)B * T * k;
   // One query per sequence: the indexer also builds the selection's first
@@ -473,8 +699,8 @@ lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers, lcs
                                                  stream),
                        "topk launch"));
       } else {
-        TRY(hip_status(lcs::launch_idx_score(ly.q8, ly.q_scale, ly.w, ly.k8, ly.k_scale, vis_len,
-                                             B, T, L, scores_scratch, stream),
+        TRY(hip_status(lcs::launch_idx_score(ly.q8, ly.q_scale, ly.w, ly.k8, ly.k_scale, L,
+                                             vis_len, B, T, L, scores_scratch, stream),
                        "idx_score launch"));
         TRY(hip_status(lcs::launch_topk(scores_scratch, vis_len, B * T, L, k, cur, ws_topk, stream),
                        "topk launch"));
@@ -482,9 +708,8 @@ lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers, lcs
     }
     // KV Share: every MTP draft step reads the first step's cache
     const lcs_layer& kvl = mtp_steps > 0 ? layers[0] : ly;
-    TRY(hip_status(lcs::launch_sparse_mla(ly.q, kvl.kv, kv_dtype == LCS_KV_FP8_E4M3, kvl.kv_scale,
-                                          cur, B, T, L, k, sm_scale, ly.out, ly.lse, ws_attn,
-                                          stream),
+    TRY(hip_status(lcs::launch_sparse_mla(ly.q, kvl.kv, fp8, kvl.kv_scale, L, cur, B, T, L, k,
+                                          sm_scale, ly.out, ly.lse, ws_attn, stream),
                    "sparse_mla launch"));
   }
   return ok();

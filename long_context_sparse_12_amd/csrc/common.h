@@ -88,9 +88,11 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---- launchers (host) ----
 
+// kstride: rows (tokens) from one sequence's keys (and key scales) to the next
 hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
-                            const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
-                            int B, int T, int L, float* scores, hipStream_t stream);
+                            const uint8_t* k8, const float* k_scale, int64_t kstride,
+                            const int32_t* vis_len, int B, int T, int L, float* scores,
+                            hipStream_t stream);
 
 hipError_t launch_idx_score_paged(const uint8_t* q8, const float* q_scale, const float* w,
                                   const uint8_t* k8, const float* k_scale,
@@ -120,9 +122,10 @@ hipError_t launch_idx_score_hist(const uint8_t* q8, const float* q_scale, const 
                                  int B, int L, float* scores, uint32_t* hist, hipStream_t stream);
 
 size_t attn_workspace_bytes(int64_t queries, int k);
+// kv_stride: rows (tokens) from one sequence's latent rows (and row scales) to the next
 hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
-                             const float* kv_scale, const int32_t* idx, int B, int T, int L,
-                             int k, float sm_scale, uint16_t* out, float* lse,
+                             const float* kv_scale, int64_t kv_stride, const int32_t* idx, int B,
+                             int T, int L, int k, float sm_scale, uint16_t* out, float* lse,
                              void* workspace, hipStream_t stream);
 
 // paged KV: kv/kv_scale are pools of 2^lbs-row blocks, block_table [B][max_blocks]

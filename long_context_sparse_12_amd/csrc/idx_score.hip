@@ -93,8 +93,8 @@ template <int TQ, bool PAGED, bool HIST = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 1 ? 4 : 2))) idx_decode_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
-    const float* __restrict__ k_scale, const int32_t* __restrict__ vis_len, int T,
-    int t0, int L, int keys_per_wg, float* __restrict__ scores,
+    const float* __restrict__ k_scale, int64_t key_stride, const int32_t* __restrict__ vis_len,
+    int T, int t0, int L, int keys_per_wg, float* __restrict__ scores,
     const int32_t* __restrict__ block_table, int max_blocks, int lbs, int n_blocks,
     uint32_t* __restrict__ hist) {
   static_assert(!HIST || (TQ == 1 && !PAGED), "the fused histogram is built for T = 1 only");
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
     __syncthreads();
   }
 
-  const int64_t key_base_b = (int64_t)b * L;
+  const int64_t key_base_b = (int64_t)b * key_stride;  // this sequence's first key row
   const int wg_begin = blockIdx.x * keys_per_wg;
   const int wg_end = min(L, wg_begin + keys_per_wg);
   const int blk0 = wg_begin >> lbs;
@@ -285,8 +285,9 @@ template <bool PAGED>
 __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k8,
-    const float* __restrict__ k_scale, const int32_t* __restrict__ vis_len, int T, int L,
-    int queries_per_wg, float* __restrict__ scores, const int32_t* __restrict__ block_table,
+    const float* __restrict__ k_scale, int64_t key_stride, const int32_t* __restrict__ vis_len,
+    int T, int L, int queries_per_wg, float* __restrict__ scores,
+    const int32_t* __restrict__ block_table,
     int max_blocks, int lbs, int n_blocks) {
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[2][kPfBufBytes];
 
@@ -299,7 +300,7 @@ __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
   const int t_end = min(T, t_begin + queries_per_wg);
   if (t_begin >= t_end) return;
 
-  const int64_t key_base_b = (int64_t)b * L;
+  const int64_t key_base_b = (int64_t)b * key_stride;
   const int kw0 = blockIdx.x * kPfKeysPerWg + wave * kPfKeysPerWave;
 
   // row of a key (clamped to L - 1): b * L + key, or its pool row (paged)
@@ -426,14 +427,17 @@ __global__ void __launch_bounds__(kPfThreads) idx_prefill_kernel(
         const int c = kb >> 1;
         const int t = c0 + qi;
         const int64_t bt = (int64_t)b * T + (t < t_end ? t : t_end - 1);
+        // the row's byte range and each key's byte offset are unsigned 32-bit
+        // values (L < 2^30 keeps 4 L below 2^32)
         const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
-            scores + bt * L, 0, t < t_end ? L * 4 : 0, kBufferWord3);
+            scores + bt * L, 0, t < t_end ? (int)(4u * (uint32_t)L) : 0, kBufferWord3);
         const int vis = clamp_vis(__builtin_amdgcn_readlane(vis_cur, qi), L);
         // lane l: key kw0 + 64 c + l (blocks 2c and 2c+1 by lane half)
         const float res = sum_pair(P[0], P[1]) * ks[c];
         const int key = kw0 + 64 * c + lane;
         const float v = key < vis ? res : -INFINITY;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out, 4 * key, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out, (int)(4u * (uint32_t)key), 0,
+                                              0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -466,7 +470,8 @@ namespace {
 
 template <bool PAGED>
 hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float* w,
-                           const uint8_t* k8, const float* k_scale, const int32_t* vis_len, int B,
+                           const uint8_t* k8, const float* k_scale, int64_t kstride,
+                           const int32_t* vis_len, int B,
                            int T, int L, float* scores, const int32_t* btab, int max_blocks,
                            int lbs, int n_blocks, uint32_t* hist, hipStream_t stream) {
   if (T >= LCS_IDX_PREFILL_MIN_T) {
@@ -480,7 +485,7 @@ hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float*
     const int per = (int)((chunks + want - 1) / want) * kPfChunk;
     const int gy = (T + per - 1) / per;
     return launch_kernel(idx_prefill_kernel<PAGED>, dim3(gx, gy, B), dim3(kPfThreads), 0, stream,
-                         q8, q_scale, w, k8, k_scale, vis_len, T, L, per, scores, btab,
+                         q8, q_scale, w, k8, k_scale, kstride, vis_len, T, L, per, scores, btab,
                          max_blocks, lbs, n_blocks);
   }
   // keys per workgroup: a multiple of 4 waves x 64 keys, sized for enough WGs
@@ -493,7 +498,7 @@ hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float*
   if (hist) {
     if (PAGED || T != 1) return hipErrorInvalidValue;
     return launch_kernel(idx_decode_kernel<1, false, true>, grid, dim3(256), 0, stream, q8,
-                         q_scale, w, k8, k_scale, vis_len, T, 0, L, kpw, scores, btab, max_blocks,
+                         q_scale, w, k8, k_scale, kstride, vis_len, T, 0, L, kpw, scores, btab, max_blocks,
                          lbs, n_blocks, hist);
   }
   for (int t0 = 0; t0 < T; t0 += kMaxTq) {
@@ -502,7 +507,8 @@ hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float*
 #define LCS_DECODE_CASE(N)                                                                      \
   case N:                                                                                       \
     e = launch_kernel(idx_decode_kernel<N, PAGED>, grid, dim3(256), 0, stream, q8, q_scale, w, k8, \
-                      k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs, n_blocks,    \
+                      k_scale, kstride, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,     \
+                      n_blocks,                                                                  \
                       nullptr);                                                                  \
     break;
     switch (tq) {
@@ -513,7 +519,7 @@ hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float*
       LCS_DECODE_CASE(5)
       default:
         e = launch_kernel(idx_decode_kernel<kMaxTq, PAGED>, grid, dim3(256), 0, stream, q8, q_scale,
-                          w, k8, k_scale, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
+                          w, k8, k_scale, kstride, vis_len, T, t0, L, kpw, scores, btab, max_blocks, lbs,
                           n_blocks, nullptr);
         break;
     }
@@ -526,17 +532,18 @@ hipError_t launch_idx_impl(const uint8_t* q8, const float* q_scale, const float*
 }  // namespace
 
 hipError_t launch_idx_score(const uint8_t* q8, const float* q_scale, const float* w,
-                            const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
-                            int B, int T, int L, float* scores, hipStream_t stream) {
-  return launch_idx_impl<false>(q8, q_scale, w, k8, k_scale, vis_len, B, T, L, scores, nullptr, 0,
-                                0, 0, nullptr, stream);
+                            const uint8_t* k8, const float* k_scale, int64_t kstride,
+                            const int32_t* vis_len, int B, int T, int L, float* scores,
+                            hipStream_t stream) {
+  return launch_idx_impl<false>(q8, q_scale, w, k8, k_scale, kstride, vis_len, B, T, L, scores,
+                                nullptr, 0, 0, 0, nullptr, stream);
 }
 
 hipError_t launch_idx_score_hist(const uint8_t* q8, const float* q_scale, const float* w,
                                  const uint8_t* k8, const float* k_scale, const int32_t* vis_len,
                                  int B, int L, float* scores, uint32_t* hist, hipStream_t stream) {
-  return launch_idx_impl<false>(q8, q_scale, w, k8, k_scale, vis_len, B, 1, L, scores, nullptr, 0,
-                                0, 0, hist, stream);
+  return launch_idx_impl<false>(q8, q_scale, w, k8, k_scale, (int64_t)L, vis_len, B, 1, L, scores,
+                                nullptr, 0, 0, 0, hist, stream);
 }
 
 hipError_t launch_idx_score_paged(const uint8_t* q8, const float* q_scale, const float* w,
@@ -544,8 +551,8 @@ hipError_t launch_idx_score_paged(const uint8_t* q8, const float* q_scale, const
                                   const int32_t* block_table, int max_blocks, int lbs,
                                   int n_blocks, const int32_t* vis_len, int B, int T, int L,
                                   float* scores, hipStream_t stream) {
-  return launch_idx_impl<true>(q8, q_scale, w, k8, k_scale, vis_len, B, T, L, scores, block_table,
-                               max_blocks, lbs, n_blocks, nullptr, stream);
+  return launch_idx_impl<true>(q8, q_scale, w, k8, k_scale, 0, vis_len, B, T, L, scores,
+                               block_table, max_blocks, lbs, n_blocks, nullptr, stream);
 }
 
 }  // namespace lcs

@@ -329,9 +329,9 @@ __device__ __forceinline__ void tile_step(AttnCtx<FP8>& c, int tile, int tid) {
 template <bool FP8>
 __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv,
-    const float* __restrict__ kv_scale, const int32_t* __restrict__ idx, int T, int L, int k,
-    int rows_per_split, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse,
-    uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
+    const float* __restrict__ kv_scale, int64_t kv_stride, const int32_t* __restrict__ idx, int T,
+    int L, int k, int rows_per_split, float sm_scale, uint16_t* __restrict__ out,
+    float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   using C = AttnCtx<FP8>;
   __shared__ __attribute__((aligned(16))) uint8_t s_st0[C::kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_st1[C::kStageBytes];
@@ -356,7 +356,7 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
   c.s_idx = s_idx;
   c.s_scl = s_scl;
   c.kv8 = (const uint8_t*)kv;
-  c.kv_b = (int64_t)b * L;
+  c.kv_b = (int64_t)b * kv_stride;  // this sequence's first row
   c.lane = tid & 63;
   c.wave = tid >> 6;
   c.hg = c.wave & 1;
@@ -398,7 +398,7 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
     for (int u = 0; u < kSclPer; ++u) {
       const int i = tid + kThreadsA * u;
       const int32_t s = i < c.n_tiles * kTileRows ? s_idx[i] : -1;
-      scl[u] = s >= 0 ? kv_scale[(int64_t)b * L + s] : 0.f;
+      scl[u] = s >= 0 ? kv_scale[c.kv_b + s] : 0.f;
     }
   }
   if (c.n_tiles > 0) issue_tile<FP8, 0>(c, 0);
@@ -539,7 +539,7 @@ struct AttnB {
   int* flag;        // [2 parity][2 hg]
   int32_t* ring;    // [4 slots][32 rows]  positions of the tiles t with t & 3 = slot
   float* sring;     // [4 slots][32 rows]  FP8 row scales of the same tiles
-  const float* kscale;   // FP8 row scales of this sequence (kv_scale + b * L), or
+  const float* kscale;   // FP8 row scales of this sequence (kv_scale + b * stride), or
                          // of the whole pool (paged)
   const int32_t* idx_q;  // this split's selected positions (global memory)
   const int32_t* btab;   // paged: this sequence's block table row
@@ -611,7 +611,7 @@ struct PWave {
 
 struct GWave {
   int g;                // 0 or 1 (wave-uniform)
-  const uint8_t* kvb;   // this sequence's rows: kv + b * L * (1152 or 576); paged: the pool
+  const uint8_t* kvb;   // this sequence's rows: kv + b * stride * (1152 or 576); paged: the pool
   int dma_row[kDmaPerB];  // row inside the tile of each gather
   int dma_off[kDmaPerB];  // byte offset inside the row (swizzled granule)
 };
@@ -625,7 +625,7 @@ struct GWave {
 constexpr int kFp8Per = kTileRows * (kKvDim / 16) / (64 * kGatherWaves);  // 9
 struct GWave8 {
   int g;
-  const uint8_t* kvb;     // kv + b * L * 576; paged: the pool
+  const uint8_t* kvb;     // kv + b * stride * 576; paged: the pool
   int row[kFp8Per];       // tile row of each granule
   int src[kFp8Per];       // byte offset inside the 576-byte row
   int dst[kFp8Per];       // stage byte offset of its first bf16 granule
@@ -928,7 +928,8 @@ __device__ __forceinline__ void s_step(const AttnB& c, SWave& w, int j) {
 template <bool FP8, bool PAGED>
 __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
     const uint16_t* __restrict__ q, const void* kv, const float* __restrict__ kv_scale,
-    const int32_t* __restrict__ idx, int T, int L, int k, int rows_per_split, float sm_scale,
+    int64_t kv_stride, const int32_t* __restrict__ idx, int T, int L, int k, int rows_per_split,
+    float sm_scale,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_lse, const int32_t* __restrict__ block_table, int max_blocks,
     int lbs, int n_blocks) {
@@ -959,7 +960,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   c.flag = s_flag;
   c.ring = s_ring;
   c.sring = s_sring;
-  c.kscale = FP8 ? (PAGED ? kv_scale : kv_scale + (int64_t)b * L) : nullptr;
+  c.kscale = FP8 ? (PAGED ? kv_scale : kv_scale + (int64_t)b * kv_stride) : nullptr;
   c.btab = PAGED ? block_table + (int64_t)b * max_blocks : nullptr;
   c.lbs = lbs;
   c.nblk = n_blocks;
@@ -1039,7 +1040,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   if (FP8 && role == kRoleGather) {
     GWave8 w;
     w.g = __builtin_amdgcn_readfirstlane(c.wave - 4);
-    w.kvb = (const uint8_t*)kv + (PAGED ? 0 : (int64_t)b * L * kKvDim);
+    w.kvb = (const uint8_t*)kv + (PAGED ? 0 : (int64_t)b * kv_stride * kKvDim);
 #pragma unroll
     for (int i = 0; i < kFp8Per; ++i) {
       const int gi = 64 * (w.g + kGatherWaves * i) + c.lane;  // FP8 granule of the tile
@@ -1070,7 +1071,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   if (!FP8 && role == kRoleGather) {
     GWave w;
     w.g = __builtin_amdgcn_readfirstlane(c.wave - 4);
-    w.kvb = (const uint8_t*)kv + (PAGED ? 0 : (int64_t)b * L * kRowBytes);
+    w.kvb = (const uint8_t*)kv + (PAGED ? 0 : (int64_t)b * kv_stride * kRowBytes);
 #pragma unroll
     for (int i = 0; i < kDmaPerB; ++i) {
       const int o = 1024 * (w.g + kGatherWaves * i) + 16 * c.lane;  // LDS byte in the stage
@@ -1270,7 +1271,8 @@ size_t attn_workspace_bytes(int64_t queries, int k) {
 }
 
 hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
-                             const float* kv_scale, const int32_t* idx, int B, int T, int L,
+                             const float* kv_scale, int64_t kv_stride, const int32_t* idx, int B,
+                             int T, int L,
                              int k, float sm_scale, uint16_t* out, float* lse,
                              void* workspace, hipStream_t stream) {
   const int64_t queries = (int64_t)B * T;
@@ -1288,18 +1290,20 @@ hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
   const int32_t* no_tab = nullptr;
   if (role_kernel && kv_fp8)
     e = launch_kernel(sparse_mla_b_kernel<true, false>, grid, dim3(kThreadsB), 0, stream, q, kv,
-                      kv_scale, idx, T, L, k, p.rows_per_split, sm_scale, out, lse, part_o,
-                      part_lse, no_tab, 0, 0, 0);
+                      kv_scale, kv_stride, idx, T, L, k, p.rows_per_split, sm_scale, out, lse,
+                      part_o, part_lse, no_tab, 0, 0, 0);
   else if (role_kernel)
     e = launch_kernel(sparse_mla_b_kernel<false, false>, grid, dim3(kThreadsB), 0, stream, q, kv,
-                      (const float*)nullptr, idx, T, L, k, p.rows_per_split, sm_scale, out, lse,
-                      part_o, part_lse, no_tab, 0, 0, 0);
+                      (const float*)nullptr, kv_stride, idx, T, L, k, p.rows_per_split, sm_scale,
+                      out, lse, part_o, part_lse, no_tab, 0, 0, 0);
   else if (kv_fp8)
-    e = launch_kernel(sparse_mla_kernel<true>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx, T,
-                      L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
+    e = launch_kernel(sparse_mla_kernel<true>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale,
+                      kv_stride, idx, T, L, k, p.rows_per_split, sm_scale, out, lse, part_o,
+                      part_lse);
   else
-    e = launch_kernel(sparse_mla_kernel<false>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale, idx,
-                      T, L, k, p.rows_per_split, sm_scale, out, lse, part_o, part_lse);
+    e = launch_kernel(sparse_mla_kernel<false>, grid, dim3(kThreadsA), 0, stream, q, kv, kv_scale,
+                      kv_stride, idx, T, L, k, p.rows_per_split, sm_scale, out, lse, part_o,
+                      part_lse);
   if (e != hipSuccess || p.splits <= 1) return e;
   return launch_split_combine(part_o, part_lse, p.splits, queries, out, lse, stream);
 }
@@ -1322,12 +1326,12 @@ hipError_t launch_sparse_mla_paged(const uint16_t* q, const void* kv, bool kv_fp
   hipError_t e;
   if (kv_fp8)
     e = launch_kernel(sparse_mla_b_kernel<true, true>, grid, dim3(kThreadsB), 0, stream, q, kv,
-                      kv_scale, idx, T, L, k, p.rows_per_split, sm_scale, out, lse, part_o,
-                      part_lse, block_table, max_blocks, lbs, n_blocks);
+                      kv_scale, (int64_t)0, idx, T, L, k, p.rows_per_split, sm_scale, out, lse,
+                      part_o, part_lse, block_table, max_blocks, lbs, n_blocks);
   else
     e = launch_kernel(sparse_mla_b_kernel<false, true>, grid, dim3(kThreadsB), 0, stream, q, kv,
-                      (const float*)nullptr, idx, T, L, k, p.rows_per_split, sm_scale, out, lse,
-                      part_o, part_lse, block_table, max_blocks, lbs, n_blocks);
+                      (const float*)nullptr, (int64_t)0, idx, T, L, k, p.rows_per_split, sm_scale,
+                      out, lse, part_o, part_lse, block_table, max_blocks, lbs, n_blocks);
   if (e != hipSuccess || p.splits <= 1) return e;
   return launch_split_combine(part_o, part_lse, p.splits, queries, out, lse, stream);
 }

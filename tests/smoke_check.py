@@ -32,18 +32,19 @@ def _one(w):
     lcs.indexshare_forward(layers_d, lcs.SCHED_GROUP4, to_dev(vis), k, w.sm_scale, scores,
                            idx_out, ws)
     torch.cuda.synchronize()
-    outs, lses, ref_idx = oracle.indexshare(layers_h, oracle.SCHED_GROUP4, vis, k, w.sm_scale)
+    _, _, ref_idx = oracle.indexshare(layers_h, oracle.SCHED_GROUP4, vis, k, w.sm_scale)
     _, s64 = oracle.idx_score(layers_h[0]["q8"], layers_h[0]["q_scale"], layers_h[0]["w"],
                               layers_h[0]["k8"], layers_h[0]["k_scale"], vis, want64=True)
-    overlap, gap = check_selection(idx_out[0].cpu().numpy(), ref_idx[0], s64)
+    got = idx_out[0].cpu().numpy()
+    overlap, gap = check_selection(got, ref_idx[0], s64)
+    # every layer's attention against the oracle over the selection the GPU made
     worst = 0.0
-    if np.array_equal(idx_out[0].cpu().numpy(), ref_idx[0]):
-        for l in range(w.n_layers):
-            _, _, o64 = oracle.sparse_mla(layers_h[l]["q"], layers_h[l]["kv"], None, ref_idx[0],
-                                          w.sm_scale, want64=True)
-            mx, _, _ = check_attention(layers_d[l]["out"], o64, layers_d[l]["lse"],
-                                       lses[l].astype(np.float64))
-            worst = max(worst, mx)
+    for l in range(w.n_layers):
+        _, l64, o64 = oracle.sparse_mla(layers_h[l]["q"], layers_h[l]["kv"], None, got,
+                                        w.sm_scale, want64=True)
+        mx, _, _ = check_attention(layers_d[l]["out"], o64, layers_d[l]["lse"],
+                                   l64.astype(np.float64))
+        worst = max(worst, mx)
     print("smoke ok: %s, selection overlap %.5f (worst gap %.2g), attention max-abs %.3g"
           % (w.name, overlap, gap, worst), flush=True)
 

@@ -37,9 +37,18 @@ def _fn(name, args, res=ctypes.c_int):
     return f
 
 
-idx_score = _fn("lcs_idx_score", [_v] * 6 + [_i] * 3 + [_v, _v])
+_l = ctypes.c_int64
+idx_score_c = _fn("lcs_idx_score", [_v] * 5 + [_l, _v] + [_i] * 3 + [_v, _v])
+
+
+def idx_score(q8, qs, w, k8, ks, vis, B, T, L, scores, stream, stride=None):
+    return idx_score_c(q8, qs, w, k8, ks, L if stride is None else stride, vis, B, T, L, scores,
+                       stream)
+
+
 topk = _fn("lcs_topk_select", [_v, _v] + [_i] * 4 + [_v, _v, _z, _v])
-attn = _fn("lcs_sparse_mla_attn", [_v, _v, ctypes.c_int, _v, _v] + [_i] * 4 + [_f, _v, _v, _v, _z, _v])
+attn = _fn("lcs_sparse_mla_attn", [_v, _v, ctypes.c_int, _v, _l, _v] + [_i] * 4
+           + [_f, _v, _v, _v, _z, _v])
 last = _fn("lcs_last_error", [], ctypes.c_char_p)
 
 
@@ -50,7 +59,28 @@ def test_idx_score_validation():
     assert idx_score(P, P, P, P, P, P, 0, 1, 64, P, None) == SHAPE
     assert idx_score(P, P, P, P, P, P, 1, 1, -5, P, None) == SHAPE
     assert idx_score(P, P, P, P, P, P, 1, 1, (1 << 30) + 1, P, None) == SHAPE
+    # a score row must span fewer than 2^32 bytes (32-bit buffer ranges and offsets)
+    assert idx_score(P, P, P, P, P, P, 1, 1, 1 << 30, P, None) == SHAPE and b"2^30" in last()
     assert idx_score(P, P, P, P, P, None, 1, 1, 64, P, None) == NULL
+
+
+def test_idx_score_batch_stride_and_aliasing():
+    G = 1 << 30  # well-separated fake buffers
+    bufs = [P + i * G for i in range(7)]
+    q8, qs, w, k8, ks, vis, sc = bufs
+    ok_args = (q8, qs, w, k8, ks, vis, 2, 1, 1000)
+    # the stride is in rows (tokens) and at least L
+    assert idx_score(*ok_args, sc, None, stride=999) == SHAPE and b"k_batch_stride" in last()
+    assert idx_score(*ok_args, sc, None, stride=-1) == SHAPE
+    assert idx_score(*ok_args, sc, None, stride=(1 << 40)) == SHAPE
+    # outputs must not overlap inputs: scores on top of the keys, the weights, the
+    # second sequence's key rows of a strided cache, and the key scales
+    assert idx_score(*ok_args, k8, None) == SHAPE
+    assert last() in (b"scores overlaps k8 (outputs must not alias other buffers)",
+                      b"k8 overlaps scores (outputs must not alias other buffers)")
+    assert idx_score(*ok_args, w + 16, None) == SHAPE and b"w" in last()
+    assert idx_score(*ok_args, k8 + 3000 * 128, None, stride=3000) == SHAPE
+    assert idx_score(*ok_args, ks + 16, None) == SHAPE and b"k_scale" in last()
 
 
 def test_topk_validation():
@@ -75,8 +105,8 @@ def test_attn_validation():
     def call(**kw):
         a = dict(args)
         a.update(kw)
-        return attn(a["q"], a["kv"], a["dt"], a["sc"], a["idx"], a["B"], a["T"], a["L"], a["k"],
-                    a["sm"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+        return attn(a["q"], a["kv"], a["dt"], a["sc"], a["L"], a["idx"], a["B"], a["T"], a["L"],
+                    a["k"], a["sm"], a["out"], a["lse"], a["ws"], a["wsb"], None)
 
     assert call(q=None) == NULL
     assert call(dt=7) == UNSUP
@@ -88,6 +118,33 @@ def test_attn_validation():
     assert call(lse=P + 8) == SHAPE
 
 
+def test_attn_batch_stride_and_aliasing():
+    G = 1 << 30
+    q, kv, sc, idx, out, lse, ws = [P + i * G for i in range(7)]
+    B, T, L, k = 2, 1, 1000, 2048
+    need = lcs.attn_workspace_bytes(B, T, k)
+
+    def call(dt=1, stride=L, **kw):
+        a = dict(q=q, kv=kv, sc=sc, idx=idx, out=out, lse=lse, ws=ws)
+        a.update(kw)
+        return attn(a["q"], a["kv"], dt, a["sc"] if dt == 1 else None, stride, a["idx"], B, T, L,
+                    k, 1 / 24, a["out"], a["lse"], a["ws"], need, None)
+    assert call(stride=L - 1) == SHAPE and b"kv_batch_stride" in last()
+    assert call(stride=(1 << 40)) == SHAPE
+    # out over the idx list, q, the rows of sequence 1 of a strided FP8 cache (row
+    # b * stride), the lse over out, the workspace over q
+    assert call(out=idx) == SHAPE and b"overlaps" in last()
+    assert call(out=q + 64 * 576 * 2 - 16) == SHAPE
+    assert call(out=kv + 5000 * 576, stride=5000) == SHAPE and b"kv" in last()
+    assert call(lse=out + 64 * 512 * 2 * 2 - 16) == SHAPE and b"lse" in last()
+    assert call(ws=q + 16) == SHAPE and b"workspace" in last()
+    # the kv_scale rows of a bf16 cache do not exist; an output where the FP8
+    # scales would be is fine, but the FP8 cache's scale rows (stride 5000) reach
+    # it: ((B - 1) * 5000 + L) * 4 bytes
+    assert call(dt=1, stride=5000, out=sc + (5000 + L) * 4 - 16) == SHAPE and \
+        b"kv_scale" in last()
+
+
 def test_quantize_validation():
     f = _fn("lcs_quantize_e4m3", [_v, ctypes.c_int64, _i, _v, _v, _v])
     assert f(P, 10, 64, P, P, None) == UNSUP and b"128 or 576" in last()
@@ -97,6 +154,9 @@ def test_quantize_validation():
     assert f(None, 4, 576, P, P, None) == NULL
     assert f(P, 4, 576, P + 8, P, None) == SHAPE
     assert f(P, 4, 128, P, None, None) == NULL
+    # codes over the input rows, scales over the codes
+    assert f(P, 4, 128, P + 16, P + (1 << 20), None) == SHAPE and b"codes" in last()
+    assert f(P, 4, 128, P + (1 << 20), P + (1 << 20) + 16, None) == SHAPE
 
 
 def test_cache_append_validation():
@@ -113,6 +173,11 @@ def test_cache_append_validation():
     assert f(P, None, 0, P, 1, 1, 8, P, P, P, None, None) == SHAPE  # kv without kv_new
     assert f(P, P, 0, P, 1, 0, 8, P, P, P, None, None) == SHAPE
     assert f(P, P, 0, P + 4, 1, 1, 8, P, P, P, None, None) == SHAPE
+    # the caches must not overlap the new rows or the positions
+    G = 1 << 30
+    assert f(P, None, 0, P + G, 1, 1, 8, P + 128, P + 3 * G, None, None, None) == SHAPE
+    assert b"k8 overlaps k_new" in last() or b"k_new" in last()
+    assert f(None, P, 1, P + G, 1, 1, 8, None, None, P + G - 576, P + 2 * G, None) == SHAPE
 
 
 def test_context_parallel_validation():
@@ -129,12 +194,15 @@ def test_context_parallel_validation():
     loc = _fn("lcs_idx_localize", [_v] + [_i] * 5 + [_v, _v])
     assert loc(P, 1, 1, 64, 10, 5, P + 256, None) == SHAPE
     assert loc(P, 1, 1, 64, 0, 5, P, None) == SHAPE and b"alias" in last()
+    assert loc(P, 1, 1, 64, 0, 5, P + 64 * 4 - 16, None) == SHAPE  # partial overlap
     assert loc(P, 0, 1, 64, 0, 5, P + 256, None) == SHAPE
     comb = _fn("lcs_lse_combine", [_v, _v] + [_i] * 3 + [_v, _v, _v])
     assert comb(P, P, 0, 1, 1, P, None, None) == SHAPE
     assert comb(P, P, 1025, 1, 1, P, None, None) == SHAPE
     assert comb(P, P, 2, 1, 1, None, None, None) == NULL
     assert comb(P, P, 2, 1, 1, P, P + 4, None) == SHAPE
+    G1 = 1 << 30
+    assert comb(P, P + G1, 2, 1, 1, P + 64 * 512 * 2, None, None) == SHAPE  # out in part_out
 
 
 class _Pg(ctypes.Structure):
@@ -196,7 +264,23 @@ def test_indexshare_validation():
     assert f(arr, 4, 0, None, 3, 0, P, B, T, Ln, k, 1 / 24, P, P, P, need, None) == SHAPE
     assert f(arr, 4, 0, None, 0, 0, P, B, T, Ln, k, 1 / 24, P, P, P, need - 1, None) == WS
     assert f(arr, 4, 0, None, 0, 0, P, B, T, Ln, k, 1 / 24, P, P, P, need, None) == NULL
-    assert b"layer 2" in last()  # every layer is validated before anything launches
+    # every layer is validated before anything launches, and the message keeps the cause
+    assert last() == b"layer 2 attention: out is NULL"
+    # outputs of the composite must not overlap any input of any layer
+    G = 1 << 30
+    for i in range(4):
+        for j, (name, _) in enumerate(L._fields_):
+            setattr(arr[i], name, P + (10 * i + j + 1) * G)
+        arr[i].kv_scale = None
+    vis, sc, io, ws = P + 60 * G, P + 61 * G, P + 62 * G, P + 63 * G
+    good = (arr, 4, 0, None, 0, 0, vis, B, T, Ln, k, 1 / 24, sc, io, ws, need, None)
+    arr[3].out = arr[1].q  # a shared layer writes over another layer's query
+    assert f(*good) == SHAPE and b"layer 3 out" in last()
+    arr[3].out = P + 70 * G
+    assert f(arr, 4, 0, None, 0, 0, vis, B, T, Ln, k, 1 / 24, arr[0].k8, io, ws, need,
+             None) == SHAPE and b"scores_scratch" in last()
+    assert f(arr, 4, 0, None, 0, 0, vis, B, T, Ln, k, 1 / 24, sc, arr[2].out, ws, need,
+             None) == SHAPE and b"idx_out" in last()
     assert f(arr, 4, 5, None, 0, 0, P, B, T, Ln, k, 1 / 24, P, P, P, need, None) == UNSUP
 
 

@@ -1,8 +1,10 @@
 """GPU parity of the paged-KV calls (through the C ABI): the same logical
 caches laid out in pools of blocks, in a random block order with garbage in
-every pool row no position maps to, must give the contiguous calls' results
-bit for bit (scores, selections, attention outputs), and the paged cache
-append must write what the oracle's append writes into the logical cache."""
+every pool row no position maps to, must give the oracle's results on the
+logical caches (scores, selections, attention outputs, under the usual
+tolerances) and the contiguous calls' results bit for bit, and the paged
+cache append must write what the oracle's append writes into the logical
+cache."""
 import sys
 
 import numpy as np
@@ -12,7 +14,7 @@ import torch
 import long_context_sparse_12_amd as lcs
 import oracle
 from synth import workloads as wl
-from tests.parity import DEV, to_dev
+from tests.parity import DEV, check_attention, check_scores, check_selection, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +78,11 @@ def test_idx_score_paged_equals_contiguous(case):
     got = torch.full((B, T, L), 7.0, dtype=torch.float32, device=DEV)
     lcs.idx_score_paged(d["q8"], d["q_scale"], d["w"], k8p, ksp, pg, vis, L, got)
     torch.cuda.synchronize()
+    inp = wl.host_indexer(w, 0)
+    _, ref64 = oracle.idx_score(inp["q8"], inp["q_scale"], inp["w"], inp["k8"], inp["k_scale"],
+                                w.vis_len(), want64=True)
+    rel = check_scores(got.cpu().numpy(), ref64)
+    _say("  against the oracle: max rel err %.3g" % rel)
     assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
 
 
@@ -110,6 +117,11 @@ def test_sparse_mla_paged_equals_contiguous(case):
     lse = torch.empty_like(lse_r)
     lcs.sparse_mla_attn_paged(q, kvp, scp, pg, idx_d, L, w.sm_scale, out, lse, ws)
     torch.cuda.synchronize()
+    kv_h, sc_h = wl.host_kv(w, 0)
+    _, ref_lse, ref64 = oracle.sparse_mla(wl.host_attn_q(w, 0), kv_h, sc_h, idx, w.sm_scale,
+                                          want64=True)
+    mx, _, lerr = check_attention(out, ref64, lse, ref_lse.astype(np.float64))
+    _say("  against the oracle: max-abs %.3g, lse err %.3g" % (mx, lerr))
     assert torch.equal(out.view(torch.int16), out_r.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), lse_r.view(torch.int32))
 
@@ -202,8 +214,26 @@ def test_paged_path_decode128k_shape():
     idx = torch.empty_like(idx_r)
     lcs.topk_select(sc, vis, k, idx, ws_t)
     out = torch.empty_like(out_r)
-    lcs.sparse_mla_attn_paged(q, kvp, None, pg, idx, L, w.sm_scale, out, None, ws_a)
+    lse = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+    lcs.sparse_mla_attn_paged(q, kvp, None, pg, idx, L, w.sm_scale, out, lse, ws_a)
     torch.cuda.synchronize()
+    # sampled sequences against the oracle on the logical caches
+    got_idx = idx.cpu().numpy()
+    vis_h = w.vis_len()
+    idx_s = np.arange(k, dtype=np.int32).reshape(1, 1, k)
+    for b in (2, 29):
+        inp = wl.host_indexer(w, 0, b0=b, nb=1)
+        s32, s64 = oracle.idx_score(inp["q8"], inp["q_scale"], inp["w"], inp["k8"],
+                                    inp["k_scale"], vis_h[b:b + 1], want64=True)
+        rel = check_scores(sc[b:b + 1].cpu().numpy(), s64, "b=%d" % b)
+        ov, gap = check_selection(got_idx[b:b + 1], oracle.topk(s32, vis_h[b:b + 1], k), s64)
+        sel = got_idx[b, 0]
+        kv_s, _ = wl.host_kv_rows(w, 0, b, sel)
+        _, ref_lse, ref64 = oracle.sparse_mla(wl.host_attn_q(w, 0, b0=b, nb=1), kv_s, None, idx_s,
+                                              w.sm_scale, want64=True)
+        mx, _, lerr = check_attention(out[b:b + 1], ref64, lse[b:b + 1], ref_lse.astype(np.float64))
+        _say("  b=%d against the oracle: scores %.3g, overlap %.5f (gap %.3g), max-abs %.3g"
+             % (b, rel, ov, gap, mx))
     assert torch.equal(sc.view(torch.int32), sc_r.view(torch.int32))
     assert torch.equal(idx, idx_r)
     assert torch.equal(out.view(torch.int16), out_r.view(torch.int16))

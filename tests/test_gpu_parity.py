@@ -73,6 +73,109 @@ def test_idx_score_matches_oracle(T):
     _say("  max rel err %.3g" % rel)
 
 
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 6])
+def test_idx_score_decode_many_tiles_per_wave(T):
+    """The key-streaming kernel with 2-6 queries per pass over rows long enough
+    that each wave scores 8 key tiles (2048 keys per workgroup), so both of its
+    register buffers and, past 4 queries, the LDS-held head weights carry
+    many tiles; B = 2 rows of 2^19 + 77 keys (a ragged last workgroup), one
+    query cut at a visible length inside a checked window. Three windows of
+    each row (start, middle, end) against the oracle."""
+    B, L = 2, (1 << 19) + 77
+    _say("case: idx_score decode many tiles T=%d L=%d" % (T, L))
+    w = wl.Workload("idx-long", seed=60 + T, B=B, T=T, L=L, n_layers=1, plant_permyriad=100)
+    rs = np.random.default_rng(100 + T)
+    vis = rs.integers(L - 3000, L + 1, size=(B, T)).astype(np.int32)
+    vis[0, 0] = L
+    vis[1, T - 1] = (1 << 18) + 1000
+    d = wl.dev_indexer(w, 0, DEV)
+    scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+    lcs.idx_score(d["q8"], d["q_scale"], d["w"], d["k8"], d["k_scale"], to_dev(vis), scores)
+    torch.cuda.synchronize()
+    del d
+    n = 4096
+    for r0 in (0, (1 << 18) - 100, L - n):
+        inp = wl.host_indexer(w, 0, key_r0=r0, key_nr=n)
+        vw = np.clip(vis.astype(np.int64) - r0, 0, n).astype(np.int32)
+        _, ref64 = oracle.idx_score(inp["q8"], inp["q_scale"], inp["w"], inp["k8"],
+                                    inp["k_scale"], vw, want64=True)
+        rel = check_scores(scores[:, :, r0:r0 + n].cpu().numpy(), ref64, "window %d" % r0)
+        _say("  window [%d, %d) max rel err %.3g" % (r0, r0 + n, rel))
+
+
+def _finite_e4m3(rs, shape):
+    """uniform over the 254 finite E4M3 codes (0x7F and 0xFF are NaN)"""
+    c = rs.integers(0, 254, size=shape)
+    return np.where(c < 0x7F, c, c + 1).astype(np.uint8)
+
+
+@pytest.mark.parametrize("T", [1, 4, 6, 16, 21])
+def test_idx_score_random_e4m3_bytes(T):
+    """Codes drawn from every finite E4M3 byte (subnormals, both zeros, the
+    largest magnitudes), positive scales spread over 2^-12 .. 2^12 and head
+    weights in [0, 1) with exact zeros, plus edge rows: keys of all +0, all
+    -0, only subnormals, all +-448; a query head of only subnormals and one
+    of -0. Both kernels (T < 16 streams the keys, T >= 16 the tiled MFMA
+    kernel) against the oracle. Head weights over 24 octaves let one head's
+    dot product decide a score, and where it cancels the matrix cores'
+    accumulation shows: the scores are held to 1e-3 of the terms' magnitude
+    there (measured: within 1e-4 of it)."""
+    B, L = 2, 3000 + 33
+    _say("case: idx_score random E4M3 bytes T=%d" % T)
+    rs = np.random.default_rng(500 + T)
+    q8 = _finite_e4m3(rs, (B, T, 32, 128))
+    k8 = _finite_e4m3(rs, (B, L, 128))
+    sub = np.concatenate([np.arange(1, 8), np.arange(0x81, 0x88)]).astype(np.uint8)
+    k8[0, 0] = 0x00
+    k8[0, 1] = 0x80
+    k8[0, 2] = rs.choice(sub, 128)
+    k8[1, 5] = rs.choice(np.array([0x7E, 0xFE], np.uint8), 128)
+    k8[1, L - 1] = rs.choice(sub, 128)
+    q8[0, 0, 3] = rs.choice(sub, 128)
+    q8[1, T - 1, 7] = 0x80
+    q_scale = np.exp2(rs.uniform(-12, 12, size=(B, T, 32))).astype(np.float32)
+    k_scale = np.exp2(rs.uniform(-12, 12, size=(B, L))).astype(np.float32)
+    wt = rs.random((B, T, 32)).astype(np.float32)
+    wt[wt < 0.1] = 0.0
+    vis = rs.integers(L - 200, L + 1, size=(B, T)).astype(np.int32)
+    _, ref64 = oracle.idx_score(q8, q_scale, wt, k8, k_scale, vis, want64=True)
+    scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+    lcs.idx_score(to_dev(q8), to_dev(q_scale), to_dev(wt), to_dev(k8), to_dev(k_scale),
+                  to_dev(vis), scores)
+    # magnitudes of the terms, decoded by torch's E4M3 cast (the head dot products
+    # cancel here, and the matrix cores accumulate with less than fp32 precision)
+    dec = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    terms = np.einsum("btj,btji,bsi->bts", wt.astype(np.float64) * q_scale, np.abs(dec[q8]),
+                      np.abs(dec[k8])) * k_scale[:, None, :]
+    got = scores.cpu().numpy()
+    rel = check_scores(got, ref64, terms=terms)
+    fin = np.isfinite(ref64)
+    over = float((np.abs(np.where(fin, got - ref64, 0)) / np.maximum(terms, 1e-300))[fin].max())
+    _say("  max rel err %.3g; largest error over the terms' magnitude %.3g" % (rel, over))
+
+
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_idx_score_strided_cache(T):
+    """Keys as a view k8[:, :L] of a cache of more positions per sequence (the
+    batch stride passed through the C ABI is the cache's, not L); the rows past
+    L hold other values and must not be read into the scores."""
+    B, L, Lmax = 3, 5000, 7000
+    _say("case: idx_score strided cache T=%d" % T)
+    w = wl.Workload("idx-strided", seed=90 + T, B=B, T=T, L=Lmax, n_layers=1, plant_permyriad=100)
+    inp = wl.host_indexer(w, 0)
+    rs = np.random.default_rng(T)
+    vis = rs.integers(L - 500, L + 1, size=(B, T)).astype(np.int32)
+    _, ref64 = oracle.idx_score(inp["q8"], inp["q_scale"], inp["w"], inp["k8"][:, :L],
+                                inp["k_scale"][:, :L], vis, want64=True)
+    k8 = to_dev(inp["k8"])
+    ks = to_dev(inp["k_scale"])
+    scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+    lcs.idx_score(to_dev(inp["q8"]), to_dev(inp["q_scale"]), to_dev(inp["w"]), k8[:, :L],
+                  ks[:, :L], to_dev(vis), scores)
+    rel = check_scores(scores.cpu().numpy(), ref64)
+    _say("  max rel err %.3g" % rel)
+
+
 def test_idx_score_prefill_full_size_sampled():
     """The chunked-prefill shape (4096 causal queries at the end of a 131072
     position cache), in the launch configuration the benchmark uses; rows
@@ -244,6 +347,33 @@ def test_sparse_mla_matches_oracle(case):
     _say("  max-abs %.3g (%.3g of rms), lse err %.3g" % (mx, ratio, lerr))
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_sparse_mla_strided_cache(fp8):
+    """Latent rows (and FP8 row scales) as a view kv[:, :L] of a cache of more
+    positions per sequence; selections reach the last row below L."""
+    B, T, L, Lmax, k = 4, 1, 3000, 4100, 2048
+    _say("case: sparse_mla strided cache fp8=%d" % fp8)
+    w = wl.Workload("attn-strided", seed=95 + fp8, B=B, T=T, L=Lmax, n_layers=1, kv_fp8=fp8)
+    q = wl.host_attn_q(w, 0)
+    kv, sc = wl.host_kv(w, 0)
+    rs = np.random.default_rng(3)
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        sel = np.sort(np.concatenate([rs.choice(L - 1, k - 1 - b, replace=False), [L - 1]]))
+        idx[b, 0, :len(sel)] = sel
+    _, ref_lse, ref64 = oracle.sparse_mla(q, kv[:, :L], None if sc is None else sc[:, :L], idx,
+                                          w.sm_scale, want64=True)
+    kv_d = to_dev(kv)
+    sc_d = None if sc is None else to_dev(sc)
+    out = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+    ws = _zeros(lcs.attn_workspace_bytes(B, T, k))
+    lcs.sparse_mla_attn(to_dev(q), kv_d[:, :L], None if sc_d is None else sc_d[:, :L], to_dev(idx),
+                        w.sm_scale, out, lse, ws)
+    mx, ratio, lerr = check_attention(out, ref64, lse, ref_lse.astype(np.float64))
+    _say("  max-abs %.3g (%.3g of rms), lse err %.3g" % (mx, ratio, lerr))
+
+
 def test_sparse_mla_empty_selection():
     _say("case: sparse_mla all -1")
     q, kv, sc, idx = _attn_inputs(2, 1, 100, 64, False, seed=5)
@@ -351,14 +481,15 @@ def _compare_composite(w, layers_h, layers_d, idx_out, sched, mtp_steps=0, mask=
                                   want64=True)
         ov, gap = check_selection(got_idx[f], ref_idx[f], s64)
         _say("  full layer %d: overlap %.5f worst gap %.3g" % (l, ov, gap))
+    # every layer's attention against the oracle over the selection the GPU made
+    # (the selection itself is checked above; attention is checked whatever it is)
     for l, ly in enumerate(layers_d):
         f = 0 if mtp_steps else sum(1 for x in full if x <= l) - 1
-        same = np.array_equal(got_idx[f], ref_idx[f])
-        if same:
-            ref = oracle.sparse_mla(layers_h[l]["q"], layers_h[0 if mtp_steps else l]["kv"],
-                                    layers_h[0 if mtp_steps else l].get("kv_scale"), ref_idx[f],
-                                    w.sm_scale, want64=True)
-            check_attention(ly["out"], ref[2], ly["lse"], ref[1].astype(np.float64))
+        src = layers_h[0 if mtp_steps else l]
+        _, ref_lse, ref64 = oracle.sparse_mla(layers_h[l]["q"], src["kv"], src.get("kv_scale"),
+                                              got_idx[f], w.sm_scale, want64=True)
+        mx, _, lerr = check_attention(ly["out"], ref64, ly["lse"], ref_lse.astype(np.float64))
+        _say("  layer %d attention max-abs %.3g, lse err %.3g" % (l, mx, lerr))
 
 
 def test_indexshare_tiny_group_end_to_end():
@@ -650,3 +781,54 @@ def test_prefill_causal_small():
     layers_h = _host_layers(w, 4, [0])
     layers_d, idx_out = _run_composite(w, layers_h, wl.SCHED_GROUP4)
     _compare_composite(w, layers_h, layers_d, idx_out, wl.SCHED_GROUP4)
+
+
+def test_composite_verify128k_full_size_sampled():
+    """The multi-token verify at full size (B=32, T=1+5 causal queries per
+    sequence at the end of a 131072-position cache, one 4-layer group, bf16
+    KV) through lcs_indexshare_forward as the benchmark launches it: the six
+    queries share one pass over the keys, 16 key tiles per wave. Sampled
+    queries against the oracle: their scores (the call leaves the full
+    layer's scores in its scratch), selections under the gap rule, and the
+    outputs of layers 0 and 3 over the GPU's selection."""
+    w = wl.WORKLOADS["verify128k"]
+    _say("case: composite full size %s" % w.name)
+    B, T, L, k = w.B, w.T, w.L, w.k
+    layers = []
+    for l in range(w.n_layers):
+        d = wl.dev_indexer(w, l, DEV) if l in w.full_layers() else {}
+        d["q"] = wl.dev_attn_q(w, l, DEV)
+        d["kv"], _ = wl.dev_kv(w, l, DEV)
+        d["out"] = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+        d["lse"] = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+        layers.append(d)
+    vis = w.vis_len()
+    idx_out = torch.empty((1, B, T, k), dtype=torch.int32, device=DEV)
+    scores = torch.empty((B, T, L), dtype=torch.float32, device=DEV)
+    ws = _zeros(lcs.indexshare_workspace_bytes(B, T, L, k))
+    lcs.indexshare_forward(layers, lcs.SCHED_GROUP4, to_dev(vis), k, w.sm_scale, scores, idx_out,
+                           ws, kv_dtype=lcs.KV_BF16)
+    torch.cuda.synchronize()
+    got = idx_out.cpu().numpy()
+    idx_s = np.arange(k, dtype=np.int32).reshape(1, 1, k)
+    for b, t in ((0, 0), (13, 3), (31, 5)):
+        inp = wl.host_indexer(w, 0, b0=b, nb=1)
+        q_sl = (slice(None), slice(t, t + 1))
+        s32, s64 = oracle.idx_score(inp["q8"][q_sl], inp["q_scale"][q_sl], inp["w"][q_sl],
+                                    inp["k8"], inp["k_scale"], vis[b:b + 1, t:t + 1], want64=True)
+        rel = check_scores(scores[b:b + 1, t:t + 1].cpu().numpy(), s64, "b=%d t=%d" % (b, t))
+        ref_idx = oracle.topk(s32, vis[b:b + 1, t:t + 1], k)
+        ov, gap = check_selection(got[0, b:b + 1, t:t + 1], ref_idx, s64)
+        _say("  b=%d t=%d scores max rel %.3g, selection overlap %.5f worst gap %.3g"
+             % (b, t, rel, ov, gap))
+        sel = got[0, b, t]
+        for l in (0, 3):
+            q_h = wl.host_attn_q(w, l, b0=b, nb=1)[:, t:t + 1]
+            kv_s, sc_s = wl.host_kv_rows(w, l, b, sel)
+            _, ref_lse, ref64 = oracle.sparse_mla(q_h, kv_s, sc_s, idx_s, w.sm_scale, want64=True)
+            mx, _, lerr = check_attention(layers[l]["out"][b:b + 1, t:t + 1], ref64,
+                                          layers[l]["lse"][b:b + 1, t:t + 1],
+                                          ref_lse.astype(np.float64))
+            _say("  b=%d t=%d layer %d max-abs %.3g, lse err %.3g" % (b, t, l, mx, lerr))
+    del layers, scores, ws
+    torch.cuda.empty_cache()
