@@ -131,6 +131,24 @@ lcs_status lcs_sparse_mla_attn(const uint16_t* q, const void* kv,
                                void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* lcs_sparse_mla_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid hipMalloc). When the selection is split over several workgroups
+ * (fewer queries than the GPU has compute units), the partial outputs go to a
+ * static device array of 20 MiB that the library holds on every GPU it runs
+ * on until the process ends; that covers any B * T with k <= 2048 whose
+ * lcs_attn_workspace_bytes(B, T, k) is at most 20 MiB (for example 32 decode
+ * queries, or 1 - 16), and larger needs return LCS_ERR_WORKSPACE. The call
+ * allocates nothing and needs no clearing (each call writes every partial it
+ * reads). Calls on one GPU share the array: two of them in flight at once on
+ * different streams race, so a caller runs them on one stream (or otherwise
+ * one after the other). Otherwise the same as lcs_sparse_mla_attn. */
+lcs_status lcs_sparse_mla_attn_noalloc(const uint16_t* q, const void* kv,
+                                       lcs_kv_dtype kv_dtype, const float* kv_scale,
+                                       int64_t kv_batch_stride, const int32_t* idx, int32_t B,
+                                       int32_t T, int32_t L, int32_t k, float sm_scale,
+                                       uint16_t* out, float* lse, hipStream_t stream);
+
 /* One layer of the composite call. The indexer fields are read only on
  * layers that run their own indexer; q/kv/out are used on every layer. */
 typedef struct {

@@ -18,6 +18,7 @@ __all__ = [
     "SCHED_GROUP4", "SCHED_GLM52", "SCHED_ALL_FULL", "SCHED_MASK", "KV_BF16", "KV_FP8_E4M3",
     "LIB_PATH", "quantize_e4m3", "cache_append", "topk_candidates", "topk_merge", "idx_localize",
     "lse_combine", "Paged", "idx_score_paged", "sparse_mla_attn_paged", "cache_append_paged",
+    "sparse_mla_attn_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblcs.so")
@@ -73,6 +74,8 @@ _c_topk = _sig("lcs_topk_select", ctypes.c_int, [_p, _p] + [_i32] * 4 + [_p, _p,
 _c_attn_ws = _sig("lcs_attn_workspace_bytes", _sz, [_i32] * 3)
 _c_attn = _sig("lcs_sparse_mla_attn", ctypes.c_int,
                [_p, _p, ctypes.c_int, _p, _i64, _p] + [_i32] * 4 + [_f32, _p, _p, _p, _sz, _p])
+_c_attn_na = _sig("lcs_sparse_mla_attn_noalloc", ctypes.c_int,
+                  [_p, _p, ctypes.c_int, _p, _i64, _p] + [_i32] * 4 + [_f32, _p, _p, _p])
 _c_count = _sig("lcs_count_full_layers", _i32, [ctypes.c_int, _i32, _p, _i32])
 _c_is_ws = _sig("lcs_indexshare_workspace_bytes", _sz, [_i32] * 4)
 _c_is = _sig("lcs_indexshare_forward", ctypes.c_int,
@@ -179,6 +182,17 @@ def sparse_mla_attn(q, kv, kv_scale, idx, sm_scale, out, lse=None, workspace=Non
                    float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                    0 if workspace is None else workspace.numel() * workspace.element_size(),
                    _stream(stream)))
+
+
+def sparse_mla_attn_noalloc(q, kv, kv_scale, idx, sm_scale, out, lse=None, stream=None):
+    """sparse_mla_attn with its split partials in the library's static scratch (no
+    workspace; calls on one GPU must not overlap in time)."""
+    B, T = q.shape[0], q.shape[1]
+    L = kv.shape[1]
+    k = idx.shape[-1]
+    _check(_c_attn_na(_ptr(q), _ptr(kv), _kv_dtype(kv), _ptr(kv_scale),
+                      _batch_stride(kv, KV_DIM, kv_scale), _ptr(idx), B, T, L, k,
+                      float(sm_scale), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def count_full_layers(sched, n_layers, full_mask=None, mtp_steps=0):

@@ -196,7 +196,7 @@ lcs_status validate_topk(const float* scores, const int32_t* vis_len, int32_t B,
 lcs_status validate_attn(const uint16_t* q, const void* kv, int kv_dtype, const float* kv_scale,
                          int64_t kv_stride, const int32_t* idx, int32_t B, int32_t T, int32_t L,
                          int32_t k, float sm_scale, const uint16_t* out, const float* lse,
-                         const void* ws, size_t ws_bytes) {
+                         const void* ws, size_t ws_bytes, bool own_workspace = false) {
   REQUIRE(q, "q");
   REQUIRE(kv, "kv");
   REQUIRE(idx, "idx");
@@ -215,7 +215,7 @@ lcs_status validate_attn(const uint16_t* q, const void* kv, int kv_dtype, const 
   if (!(sm_scale > 0.f) || sm_scale != sm_scale || sm_scale > 1e30f)
     return fail(LCS_ERR_SHAPE, "sm_scale must be a finite positive number");
   const size_t need = lcs::attn_workspace_bytes((int64_t)B * T, k);
-  if (need > 0) {
+  if (need > 0 && !own_workspace) {
     if (!ws) return fail(LCS_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (!aligned16(ws)) return fail(LCS_ERR_SHAPE, "workspace is not 16-byte aligned");
     if (ws_bytes < need)
@@ -386,6 +386,36 @@ lcs_status lcs_sparse_mla_attn(const uint16_t* q, const void* kv, lcs_kv_dtype k
   TRY(hip_status(lcs::launch_sparse_mla(q, kv, kv_dtype == LCS_KV_FP8_E4M3, kv_scale,
                                         kv_batch_stride, idx, B, T, L, k, sm_scale, out, lse,
                                         workspace, stream),
+                 "sparse_mla launch"));
+  return ok();
+}
+
+lcs_status lcs_sparse_mla_attn_noalloc(const uint16_t* q, const void* kv, lcs_kv_dtype kv_dtype,
+                                       const float* kv_scale, int64_t kv_batch_stride,
+                                       const int32_t* idx, int32_t B, int32_t T, int32_t L,
+                                       int32_t k, float sm_scale, uint16_t* out, float* lse,
+                                       hipStream_t stream) {
+  TRY(check_dims(B, T, L));
+  TRY(check_k(k));
+  const size_t need = lcs::attn_workspace_bytes((int64_t)B * T, k);
+  if (need > lcs::kNoAllocScratchBytes)
+    return fail(LCS_ERR_WORKSPACE,
+                "%d queries x k = %d need %zu bytes of split scratch; the static scratch holds "
+                "%zu (use lcs_sparse_mla_attn with a workspace)",
+                B * T, k, need, lcs::kNoAllocScratchBytes);
+  // the static scratch stands in for the workspace (no overlap with the caller's buffers)
+  TRY(validate_attn(q, kv, (int)kv_dtype, kv_scale, kv_batch_stride, idx, B, T, L, k, sm_scale,
+                    out, lse, nullptr, 0, /*own_workspace=*/true));
+  Regions g;
+  attn_regions(g, q, kv, kv_dtype == LCS_KV_FP8_E4M3, kv_scale, kv_batch_stride, B, T, L, out,
+               lse);
+  g.in(idx, (size_t)B * T * k * 4, "idx");
+  TRY(g.check());
+  void* ws = nullptr;
+  if (need > 0) TRY(hip_status(lcs::noalloc_scratch(&ws), "static scratch lookup"));
+  TRY(hip_status(lcs::launch_sparse_mla(q, kv, kv_dtype == LCS_KV_FP8_E4M3, kv_scale,
+                                        kv_batch_stride, idx, B, T, L, k, sm_scale, out, lse, ws,
+                                        stream),
                  "sparse_mla launch"));
   return ok();
 }

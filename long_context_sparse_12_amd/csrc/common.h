@@ -122,6 +122,10 @@ hipError_t launch_idx_score_hist(const uint8_t* q8, const float* q_scale, const 
                                  int B, int L, float* scores, uint32_t* hist, hipStream_t stream);
 
 size_t attn_workspace_bytes(int64_t queries, int k);
+// the static scratch of the allocation-free attention call: its size, and its
+// address on the current device (looked up once per device)
+constexpr size_t kNoAllocScratchBytes = (size_t)20 << 20;
+hipError_t noalloc_scratch(void** ptr);
 // kv_stride: rows (tokens) from one sequence's latent rows (and row scales) to the next
 hipError_t launch_sparse_mla(const uint16_t* q, const void* kv, bool kv_fp8,
                              const float* kv_scale, int64_t kv_stride, const int32_t* idx, int B,

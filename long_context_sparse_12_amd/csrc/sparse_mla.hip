@@ -20,6 +20,8 @@
 // With more than one split, normalised partial outputs (bf16: the final output
 // is bf16 too, and rounding the partials adds at most 2^-8 relative error) and
 // their log-sum-exp (fp32) are combined by a second kernel.
+#include <mutex>
+
 #include "common.h"
 
 namespace lcs {
@@ -1258,6 +1260,36 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
 }
 
 }  // namespace
+
+// Static scratch of lcs_sparse_mla_attn_noalloc: the split partials of one
+// call (bf16 outputs + fp32 lse of every split), for callers that cannot
+// allocate. Every GPU the library runs on holds one copy until the process
+// ends; calls on one GPU share it. In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device is current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t attn_workspace_bytes(int64_t queries, int k) {
   // the larger of the two kernels' split plans (the size query has no KV type)

@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_every_declared_function():
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -143,6 +143,27 @@ def test_attn_batch_stride_and_aliasing():
     # it: ((B - 1) * 5000 + L) * 4 bytes
     assert call(dt=1, stride=5000, out=sc + (5000 + L) * 4 - 16) == SHAPE and \
         b"kv_scale" in last()
+
+
+def test_attn_noalloc_validation():
+    f = _fn("lcs_sparse_mla_attn_noalloc", [_v, _v, ctypes.c_int, _v, _l, _v] + [_i] * 4
+            + [_f, _v, _v, _v])
+    limit = 20 << 20
+    # the split partials of up to 32 decode queries fit the static scratch, those of
+    # 255 queries (two splits each) do not; one split per query needs none
+    assert lcs.attn_workspace_bytes(32, 1, 2048) <= limit
+    assert lcs.attn_workspace_bytes(2, 1, 2048) <= limit
+    assert lcs.attn_workspace_bytes(255, 1, 2048) > limit
+    assert lcs.attn_workspace_bytes(256, 1, 2048) == 0
+    G = 1 << 30
+    q, kv, idx, out = P, P + G, P + 2 * G, P + 3 * G
+    assert f(q, kv, 0, None, 1000, idx, 255, 1, 1000, 2048, 1 / 24, out, None, None) == WS
+    assert b"static scratch" in last()
+    assert f(q, kv, 0, None, 1000, idx, 6, 40, 1000, 2048, 1 / 24, out, None, None) == WS
+    assert f(None, kv, 0, None, 1000, idx, 2, 1, 1000, 2048, 1 / 24, out, None, None) == NULL
+    assert f(q, kv, 0, None, 999, idx, 2, 1, 1000, 2048, 1 / 24, out, None, None) == SHAPE
+    assert f(q, kv, 0, None, 1000, idx, 2, 1, 1000, 2048, 1 / 24, q + 64, None, None) == SHAPE
+    assert f(q, kv, 0, None, 1000, idx, 2, 1, 1000, 4096, 1 / 24, out, None, None) == UNSUP
 
 
 def test_quantize_validation():
