@@ -78,7 +78,8 @@ __device__ __forceinline__ float sum_pair(float x, float y) {
 // and block_table [B][max_blocks] maps a sequence's blocks to pool blocks. A
 // 64-key tile starts at a multiple of 64, so it lies in one block; the
 // workgroup's slice of the table (at most 65 entries) sits in LDS.
-constexpr int kMaxWgBlocks = LCS_IDX_MAX_ITERS * kWaves * kSuper / 64 + 1;
+constexpr int kMaxWgKeys = LCS_IDX_MAX_ITERS * kWaves * kSuper;  // keys per workgroup, at most
+constexpr int kMaxWgBlocks = kMaxWgKeys / 64 + 1;
 // Up to kMaxTq queries share each key tile, so a multi-token verify of up to
 // 6 tokens reads the keys once. Past 4 queries the combined head weights
 // (w * q_scale, 16 per lane and query) move from registers to LDS, which the
@@ -99,13 +100,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
     uint32_t* __restrict__ hist) {
   static_assert(!HIST || (TQ == 1 && !PAGED), "the fused histogram is built for T = 1 only");
   constexpr bool kWqLds = TQ > 4;
+  // One query per launch: the workgroup's scores (at most 4096, 16 KB) are
+  // kept in LDS and written in one burst at its end. Stores spread through
+  // the key stream cost more than their 3 % of the bytes (measured: 109.1 ->
+  // 106.5 us per 128K decode launch, 53.7 -> 51.8 us at 1M).
+  constexpr bool kSBuf = TQ == 1;
+  __shared__ float s_sc[kSBuf ? kMaxWgKeys : 1];
   __shared__ int32_t s_blk[PAGED ? kMaxWgBlocks : 1];
   // [query][lane half][16]: the weights of the 16 heads a lane half holds
   __shared__ __attribute__((aligned(16))) float s_wq[kWqLds ? TQ * 2 * 16 : 1];
   __shared__ uint32_t s_hist[HIST ? kHistBins : 1];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // uniform, so a scalar register: nothing per lane is held across the key loop
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int ln = lane & 31, hh = lane >> 5;
   if (HIST) {
     for (int i = threadIdx.x; i < kHistBins; i += 256) s_hist[i] = 0u;
@@ -153,7 +161,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
   }
 
   int base = wg_begin + wave * kSuper;
-  if (!HIST && base >= wg_end) return;
+  if (!HIST && !kSBuf && base >= wg_end) return;
 
   // keys [tile_base + 32 blk + ln], K halves 0 and 1, and the scale of key
   // tile_base + lane
@@ -211,7 +219,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
       if (my_key < wg_end) {
         const int64_t bt = (int64_t)b * T + t0 + t;
         const float v = res * ks;
-        scores[bt * L + my_key] = my_key < vis[t] ? v : -INFINITY;
+        if (kSBuf)
+          s_sc[my_key - wg_begin] = my_key < vis[t] ? v : -INFINITY;
+        else
+          scores[bt * L + my_key] = my_key < vis[t] ? v : -INFINITY;
         if (HIST && my_key < vis[t]) atomicAdd(&s_hist[score_key(v) >> 20], 1u);
       }
       // past 4 queries, one query's MFMA results at a time (the scheduler
@@ -240,12 +251,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TQ == 
       if (base >= wg_end) break;
     }
   }
-  if (HIST) {
+  if (HIST || kSBuf) {
     __syncthreads();
-    uint32_t* rh = hist + (size_t)b * kHistBins;
     // the thread index rebuilt from the wave index (uniform) and the lane
     // count, so that no register holds it across the key loop
-    const int tid = (__builtin_amdgcn_readfirstlane(wave) << 6) +
+    const int tid = (wave << 6) +
+                    (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    if (kSBuf) {
+      float* row = scores + ((int64_t)b * T + t0) * L + wg_begin;  // TQ = 1: query t0
+      for (int i = tid; i < wg_end - wg_begin; i += 256) row[i] = s_sc[i];
+    }
+  }
+  if (HIST) {
+    uint32_t* rh = hist + (size_t)b * kHistBins;
+    const int tid = (wave << 6) +
                     (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     for (int i = tid; i < kHistBins; i += 256) {
       const uint32_t c = s_hist[i];

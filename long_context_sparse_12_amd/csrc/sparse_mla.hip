@@ -986,11 +986,12 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
     w.c_log = sm_scale * kLog2e;
     w.m_run = -INFINITY;
     w.l_run = 0.f;
-    const uint16_t* qh = q + ((int64_t)qi * kAttHeads + 32 * c.hg + (c.lane & 31)) * kKvDim +
-                         8 * (c.lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks) w.qT[ks] = as_v8bf(*(const v4i*)(qh + 16 * ks));
-    int32_t p0 = 0, p1 = 0, p2 = 0;
+    // The selected positions go out first and are published as soon as they
+    // land: the gathers wait on them. The query (36 KB per wave) is needed
+    // only from the first tile step on, so its loads stay in flight across
+    // the setup barrier, behind the positions (the memory counter completes
+    // in issue order, so waiting for a position does not wait for the query).
+    int32_t p0 = 0, p1 = 0, p2 = 0, b0 = 0, b1 = 0, b2 = 0;
     if (c.wave == 0) {
       // tiles 0..2 into the ring before the gathers start; tile 3 goes in at step -1
       p0 = load_pos(c, 0);
@@ -998,11 +999,22 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
       p2 = load_pos(c, 2);
       w.pn = load_pos(c, 3);
       if (PAGED) {
-        // pool rows of tiles 0..2; tile 3's blocks and tile 4's positions
-        // for step -1
+        // blocks of tiles 0..2; tile 3's blocks and tile 4's positions for step -1
         w.pn2 = load_pos(c, 4);
-        const int32_t b0 = load_blk(c, p0), b1 = load_blk(c, p1), b2 = load_blk(c, p2);
+        b0 = load_blk(c, p0);
+        b1 = load_blk(c, p1);
+        b2 = load_blk(c, p2);
         w.bn = load_blk(c, w.pn);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the query loads issue after these
+    const uint16_t* qh = q + ((int64_t)qi * kAttHeads + 32 * c.hg + (c.lane & 31)) * kKvDim +
+                         8 * (c.lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) w.qT[ks] = as_v8bf(*(const v4i*)(qh + 16 * ks));
+    __builtin_amdgcn_sched_barrier(0);
+    if (c.wave == 0) {
+      if (PAGED) {
         p0 = pool_row(c, p0, b0);
         p1 = pool_row(c, p1, b1);
         p2 = pool_row(c, p2, b2);
@@ -1011,8 +1023,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
       ring_put(c, 1, p1);
       ring_put(c, 2, p2);
     }
-    wait_vm<0>();
-    __syncthreads();
+    lds_barrier();  // setup: the ring holds tiles 0..2 (the query may still be loading)
     if (FP8 && c.wave == 0) {
       // scales of tiles 0 and 1 (they need the positions) land while the
       // gather waves fetch tile 0; tile 2's go in at step -1
