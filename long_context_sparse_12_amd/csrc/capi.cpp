@@ -296,7 +296,7 @@ lcs_status validate_paged(const lcs_paged* pg, int32_t L, int* lbs) {
   return LCS_OK;
 }
 
-bool is_full_layer(lcs_sched sched, int32_t l, const uint8_t* mask) {
+bool is_full_layer(int sched, int32_t l, const uint8_t* mask) {
   switch (sched) {
     case LCS_SCHED_GROUP4:
       return l % 4 == 0;
@@ -310,13 +310,25 @@ bool is_full_layer(lcs_sched sched, int32_t l, const uint8_t* mask) {
   return false;
 }
 
+// An enum argument from a C caller can hold any int, and in C++ loading an
+// enum object whose value lies outside the enum's range is undefined: the
+// entry points read each enum argument's bytes as an int before looking at it.
+template <class E>
+int enum_bits(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
 extern "C" {
 
-const char* lcs_status_string(lcs_status s) {
+const char* lcs_status_string(lcs_status s_arg) {
+  const int s = enum_bits(s_arg);
   switch (s) {
     case LCS_OK: return "ok";
     case LCS_ERR_NULL: return "null pointer";
@@ -370,11 +382,12 @@ size_t lcs_attn_workspace_bytes(int32_t B, int32_t T, int32_t k) {
   return lcs::attn_workspace_bytes((int64_t)B * T, k);
 }
 
-lcs_status lcs_sparse_mla_attn(const uint16_t* q, const void* kv, lcs_kv_dtype kv_dtype,
+lcs_status lcs_sparse_mla_attn(const uint16_t* q, const void* kv, lcs_kv_dtype kv_dtype_arg,
                                const float* kv_scale, int64_t kv_batch_stride, const int32_t* idx,
                                int32_t B, int32_t T, int32_t L, int32_t k, float sm_scale,
                                uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
+  const int kv_dtype = enum_bits(kv_dtype_arg);
   TRY(validate_attn(q, kv, (int)kv_dtype, kv_scale, kv_batch_stride, idx, B, T, L, k, sm_scale,
                     out, lse, workspace, workspace_bytes));
   Regions g;
@@ -390,11 +403,12 @@ lcs_status lcs_sparse_mla_attn(const uint16_t* q, const void* kv, lcs_kv_dtype k
   return ok();
 }
 
-lcs_status lcs_sparse_mla_attn_noalloc(const uint16_t* q, const void* kv, lcs_kv_dtype kv_dtype,
+lcs_status lcs_sparse_mla_attn_noalloc(const uint16_t* q, const void* kv, lcs_kv_dtype kv_dtype_arg,
                                        const float* kv_scale, int64_t kv_batch_stride,
                                        const int32_t* idx, int32_t B, int32_t T, int32_t L,
                                        int32_t k, float sm_scale, uint16_t* out, float* lse,
                                        hipStream_t stream) {
+  const int kv_dtype = enum_bits(kv_dtype_arg);
   TRY(check_dims(B, T, L));
   TRY(check_k(k));
   const size_t need = lcs::attn_workspace_bytes((int64_t)B * T, k);
@@ -440,9 +454,11 @@ lcs_status lcs_quantize_e4m3(const uint16_t* x, int64_t rows, int32_t D, uint8_t
   return ok();
 }
 
-lcs_status lcs_cache_append(const uint16_t* k_new, const uint16_t* kv_new, lcs_kv_dtype kv_dtype,
-                            const int32_t* pos, int32_t B, int32_t T, int32_t L, uint8_t* k8,
-                            float* k_scale, void* kv, float* kv_scale, hipStream_t stream) {
+lcs_status lcs_cache_append(const uint16_t* k_new, const uint16_t* kv_new,
+                            lcs_kv_dtype kv_dtype_arg, const int32_t* pos, int32_t B, int32_t T,
+                            int32_t L, uint8_t* k8, float* k_scale, void* kv, float* kv_scale,
+                            hipStream_t stream) {
+  const int kv_dtype = enum_bits(kv_dtype_arg);
   TRY(validate_append(k_new, kv_new, (int)kv_dtype, pos, B, T, L, k8, k_scale, kv, kv_scale));
   const size_t rows = (size_t)B * L;
   TRY(check_append_regions(k_new, kv_new, kv_dtype, pos, B, T, k8, rows * LCS_IDX_DIM, k_scale,
@@ -571,11 +587,12 @@ lcs_status lcs_idx_score_paged(const uint8_t* q8, const float* q_scale, const fl
 }
 
 lcs_status lcs_sparse_mla_attn_paged(const uint16_t* q, const void* kv_pool,
-                                     lcs_kv_dtype kv_dtype, const float* kv_scale_pool,
+                                     lcs_kv_dtype kv_dtype_arg, const float* kv_scale_pool,
                                      const lcs_paged* paged, const int32_t* idx, int32_t B,
                                      int32_t T, int32_t L, int32_t k, float sm_scale,
                                      uint16_t* out, float* lse, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream) {
+  const int kv_dtype = enum_bits(kv_dtype_arg);
   TRY(validate_attn(q, kv_pool, (int)kv_dtype, kv_scale_pool, L, idx, B, T, L, k, sm_scale, out,
                     lse, workspace, workspace_bytes));
   int lbs = 0;
@@ -601,10 +618,11 @@ lcs_status lcs_sparse_mla_attn_paged(const uint16_t* q, const void* kv_pool,
 }
 
 lcs_status lcs_cache_append_paged(const uint16_t* k_new, const uint16_t* kv_new,
-                                  lcs_kv_dtype kv_dtype, const int32_t* pos, int32_t B, int32_t T,
-                                  int32_t L, const lcs_paged* paged, uint8_t* k8_pool,
+                                  lcs_kv_dtype kv_dtype_arg, const int32_t* pos, int32_t B,
+                                  int32_t T, int32_t L, const lcs_paged* paged, uint8_t* k8_pool,
                                   float* k_scale_pool, void* kv_pool, float* kv_scale_pool,
                                   hipStream_t stream) {
+  const int kv_dtype = enum_bits(kv_dtype_arg);
   TRY(validate_append(k_new, kv_new, (int)kv_dtype, pos, B, T, L, k8_pool, k_scale_pool, kv_pool,
                       kv_scale_pool));
   int lbs = 0;
@@ -624,8 +642,9 @@ lcs_status lcs_cache_append_paged(const uint16_t* k_new, const uint16_t* kv_new,
   return ok();
 }
 
-int32_t lcs_count_full_layers(lcs_sched sched, int32_t n_layers, const uint8_t* full_mask,
+int32_t lcs_count_full_layers(lcs_sched sched_arg, int32_t n_layers, const uint8_t* full_mask,
                               int32_t mtp_steps) {
+  const int sched = enum_bits(sched_arg);
   if (n_layers <= 0 || mtp_steps < 0) return -1;
   if (mtp_steps > 0) return mtp_steps == n_layers ? 1 : -1;
   if ((int)sched < 0 || (int)sched > 3) return -1;
@@ -641,12 +660,14 @@ size_t lcs_indexshare_workspace_bytes(int32_t B, int32_t T, int32_t L, int32_t k
          align256(lcs::attn_workspace_bytes((int64_t)B * T, k));
 }
 
-lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers, lcs_sched sched,
+lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers, lcs_sched sched_arg,
                                   const uint8_t* full_mask, int32_t mtp_steps,
-                                  lcs_kv_dtype kv_dtype, const int32_t* vis_len, int32_t B,
+                                  lcs_kv_dtype kv_dtype_arg, const int32_t* vis_len, int32_t B,
                                   int32_t T, int32_t L, int32_t k, float sm_scale,
                                   float* scores_scratch, int32_t* idx_out, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
+  const int sched = enum_bits(sched_arg);
+  const int kv_dtype = enum_bits(kv_dtype_arg);
   if (!layers) return fail(LCS_ERR_NULL, "layers is NULL");
   if (n_layers <= 0) return fail(LCS_ERR_SHAPE, "n_layers must be positive");
   if (mtp_steps < 0) return fail(LCS_ERR_SHAPE, "mtp_steps must be >= 0");
