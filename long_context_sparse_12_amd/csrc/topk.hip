@@ -25,7 +25,8 @@
 //           tau and how many keys equal to tau are kept (the lowest positions),
 //           then writes each thread's selected entries at its block prefix of
 //           selection counts, i.e. in position order.
-// Scores are read twice; the lists carry the keys, so no score is gathered.
+// The chunked launches read the scores twice; the lists carry the keys, so no
+// score is gathered. The row kernel (below) reads them once in the common case.
 #include "common.h"
 
 namespace lcs {
@@ -520,32 +521,44 @@ __global__ void __launch_bounds__(kThreads) topk_final_kernel(
 
 // ---------------------------------------------------------------------------
 // One workgroup per row, for rows of at most kRowMaxL positions: the four
-// launches above in one, with the candidate lists in LDS. Histogram of the top
-// 12 key bits (coalesced loads, a thread's 8 in flight before its atomics),
-// the threshold bucket b1, then every wave compacts its own contiguous eighth
-// of the row in position order (a ballot per 64 positions) into its LDS list
-// (kRowCap entries: position | sure flag, and the key); entries past kRowCap
-// go to the wave's slice of `spill` (positions only; their keys are re-read
-// from the scores). Two more digits (12 + 8 bits) over the candidates fix the
-// threshold key tau and how many keys equal to tau are kept, and the lists are
-// emitted in wave order (= position order): the keys above tau and the first
-// ties. Each row's scores are read twice, from one CU: a single workgroup
-// keeps at most ~64 KB of loads in flight, so the row kernel pays only where
-// many rows fill the chip (chunked prefill); a few long rows (decode) use the
-// chunked launches, which spread each row over many CUs.
-constexpr int kRowCap = 2048;
-#ifndef LCS_ROW_PER1
-#define LCS_ROW_PER1 16  // scores per thread per step of the histogram pass
-#endif
+// launches above in one, with the candidate lists in LDS, and the row's
+// scores read once in the common case. Every wave walks its own contiguous
+// eighth of the row in position order (coalesced loads, two steps in flight).
+// The waves' first steps (8 x 1024 positions) form a sample: their histogram
+// of the top 12 key bits gives a bucket b_est below which the k-th largest key
+// almost surely does not lie (the sample's rank 1.5x the expected share of the
+// k best, plus 32; the exact bucket when the sample is the whole row).
+// The pass compacts every position whose bucket is at least b_est into the
+// wave's LDS list (kRowCap entries: position and key; entries past kRowCap go
+// to the wave's slice of `spill`, positions only, their keys re-read from the
+// scores), with no histogram atomics. If the lists hold at least k keys, the
+// k-th largest lies in a bucket >= b_est, where the lists' histogram is the
+// row's, so the threshold bucket b1 and the count above it come from the
+// listed keys alone (keys below b1 are passed over later). Otherwise the
+// sample over-estimated, and the row is read twice more: a histogram pass for
+// b1, then a compaction with b1. Two more digits
+// (12 + 8 bits) over the bucket-b1 entries fix the threshold key tau and how
+// many keys equal to tau are kept, and the lists are emitted in wave order
+// (= position order): the keys above tau and the first ties. A single
+// workgroup keeps at most ~64 KB of loads in flight, so the row kernel pays
+// only where many rows fill the chip (chunked prefill); a few long rows
+// (decode) use the chunked launches, which spread each row over many CUs.
+// LDS list entries per wave (8 waves: 10240): positions as 16-bit offsets in
+// the wave's segment (at most kRowMaxL / 8 = 32768 positions) and 32-bit keys,
+// so that the workgroup's LDS stays under half of the CU's and two workgroups
+// share a CU (one's list phases overlap the other's pass over its row)
+constexpr int kRowCap = 1280;
+constexpr int kRowBufWord3 = 0x00020000;  // buffer resource word 3 (gfx9): 32-bit data format
 #ifndef LCS_ROW_PER2
-#define LCS_ROW_PER2 16  // scores per lane per step of the compaction pass
-#endif  // LDS list entries per wave (8 waves: 16384)
+#define LCS_ROW_PER2 16  // scores per lane per step
+#endif
 
-__global__ void __launch_bounds__(kThreads) topk_row_kernel(
+// (four waves per SIMD: two workgroups of eight waves per CU)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) topk_row_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ vis_len, int L, int k,
     int spill_stride, uint32_t* __restrict__ spill, int32_t* __restrict__ idx) {
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t s_ent[kWavesTk][kRowCap];
+  __shared__ uint16_t s_off[kWavesTk][kRowCap];
   __shared__ uint32_t s_key[kWavesTk][kRowCap];
   __shared__ uint32_t s_scan[kThreads + kWavesTk];
   __shared__ uint32_t s_out[3];
@@ -560,115 +573,161 @@ __global__ void __launch_bounds__(kThreads) topk_row_kernel(
     return;
   }
   const float* srow = scores + (size_t)row * L;
-
-  // ---- pass 1: histogram of key bits 31..20 ----
   for (int i = tid; i < kBins1; i += kThreads) hist[i] = 0;
   __syncthreads();
-  // kPer loads of a thread per step, in two register buffers used in turn:
-  // the next step's loads are issued before this step's atomics, so two
-  // steps are in flight. The loads are unconditional (positions past the end
-  // read the row's last score, vis >= 2 here, and are not counted), so the
-  // wait before a step's atomics covers that step's loads only.
-  constexpr int kPer = LCS_ROW_PER1;
-  constexpr int kStep1 = kThreads * kPer;
-  float va[kPer], vb[kPer];
-  auto load1 = [&](float (&v)[kPer], int base) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) v[j] = srow[min(base + kThreads * j + tid, vis - 1)];
-  };
-  auto count1 = [&](const float (&v)[kPer], int base) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (base + kThreads * j + tid < vis) atomicAdd(&hist[score_key(v[j]) >> 20], 1u);
-  };
-  load1(va, 0);
-  for (int base = 0;;) {
-    load1(vb, base + kStep1);
-    count1(va, base);
-    base += kStep1;
-    if (base >= vis) break;
-    load1(va, base + kStep1);
-    count1(vb, base);
-    base += kStep1;
-    if (base >= vis) break;
-  }
-  __syncthreads();
-  select_bucket<kBins1>(hist, (uint32_t)k, s_scan, s_out);
-  const uint32_t b1 = s_out[0];
-  const uint32_t n_above = s_out[1];
 
-  // ---- pass 2: ordered compaction, wave w over positions [w seg, (w+1) seg) ----
+  // wave w walks positions [w seg, (w+1) seg) in steps of kStep positions
   const int seg = (vis + kWavesTk - 1) / kWavesTk;
   const int seg_cap = spill_stride / kWavesTk;  // >= seg: spill_stride >= L, a multiple of 8
   const int p0 = wave * seg, p1 = min(vis, p0 + seg);
   uint32_t* my_spill = spill + (size_t)row * spill_stride + (size_t)wave * seg_cap;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   uint32_t cnt = 0;
-  // kPer2 loads of a lane per step, in two register buffers used in turn as
-  // in pass 1 (positions past the segment read a valid score, not kept)
-  constexpr int kPer2 = LCS_ROW_PER2;
-  constexpr int kStep2 = 64 * kPer2;
-  float wa[kPer2], wb[kPer2];
-  auto load2 = [&](float (&v)[kPer2], int base) {
+  // kPer loads of a lane per step, in two register buffers used in turn: the
+  // next step's loads are issued before this step's atomics and ballots. The
+  // loads are unconditional buffer loads over the row's vis scores (one
+  // offset register; positions past the row read 0 and positions past the
+  // segment are neither counted nor kept), so the wait before a step covers
+  // that step's loads only.
+  constexpr int kPer = LCS_ROW_PER2;
+  constexpr int kStep = 64 * kPer;
+  const __amdgpu_buffer_rsrc_t rrow = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)srow, 0, (int)(4u * (uint32_t)vis), kRowBufWord3);
+  float va[kPer], vb[kPer];
+  auto load = [&](float (&v)[kPer], int base) {
+    const int off = 4 * (base + lane);  // < 4 (vis + 2 kStep) < 2^31
 #pragma unroll
-    for (int j = 0; j < kPer2; ++j) v[j] = srow[min(base + 64 * j + lane, vis - 1)];
+    for (int j = 0; j < kPer; ++j)
+      v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rrow, off + 256 * j, 0, 0));
   };
-  auto compact2 = [&](const float (&v)[kPer2], int base) {
+  // histogram (count) and/or ordered compaction of the keys in buckets >= bmin
+  auto step = [&](const float (&v)[kPer], int base, bool count, bool keep, uint32_t bmin) {
 #pragma unroll
-    for (int j = 0; j < kPer2; ++j) {
+    for (int j = 0; j < kPer; ++j) {
       const int p = base + 64 * j + lane;
       const uint32_t key = score_key(v[j]);
-      const bool q = p < p1 && (key >> 20) >= b1;
-      const uint64_t m = __ballot(q);
-      if (q) {
-        const uint32_t slot = cnt + (uint32_t)__popcll(m & lt);
-        const uint32_t e = (uint32_t)p | ((key >> 20) > b1 ? kSure : 0u);
-        if (slot < (uint32_t)kRowCap) {
-          s_ent[wave][slot] = e;
-          s_key[wave][slot] = key;
-        } else {
-          my_spill[slot] = e;
+      const bool valid = p < p1;
+      if (count && valid) atomicAdd(&hist[key >> 20], 1u);
+      if (keep) {
+        const bool q = valid && (key >> 20) >= bmin;
+        const uint64_t m = __ballot(q);
+        if (q) {
+          const uint32_t slot = cnt + (uint32_t)__popcll(m & lt);
+          if (slot < (uint32_t)kRowCap) {
+            s_off[wave][slot] = (uint16_t)(p - p0);
+            s_key[wave][slot] = key;
+          } else {
+            my_spill[slot] = (uint32_t)p;
+          }
         }
+        cnt += (uint32_t)__popcll(m);
       }
-      cnt += (uint32_t)__popcll(m);
     }
   };
-  if (p0 < p1) {
-    load2(wa, p0);
-    for (int base = p0;;) {
-      load2(wb, base + kStep2);
-      compact2(wa, base);
-      base += kStep2;
-      if (base >= p1) break;
-      load2(wa, base + kStep2);
-      compact2(wb, base);
-      base += kStep2;
-      if (base >= p1) break;
-    }
+
+  // ---- the sample: every wave's first step ----
+  load(va, p0);
+  load(vb, p0 + kStep);
+  step(va, p0, true, false, 0u);
+  __syncthreads();
+  uint32_t sample = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesTk; ++w) sample += (uint32_t)max(0, min(kStep, min(vis, w * seg + seg) - w * seg));
+  uint32_t need_est = (uint32_t)k;
+  if (sample < (uint32_t)vis) {
+    const uint64_t share = ((uint64_t)k * sample + (uint64_t)vis - 1) / (uint64_t)vis;
+    need_est = (uint32_t)min<uint64_t>((uint64_t)sample, (3 * share + 1) / 2 + 32);
+  }
+  select_bucket<kBins1>(hist, need_est, s_scan, s_out);
+  const uint32_t b_est = s_out[0];
+
+  // ---- the rest of the pass: compaction above b_est (no histogram) ----
+  step(va, p0, false, true, b_est);
+  for (int base = p0 + kStep; base < p1;) {
+    load(va, base + kStep);
+    step(vb, base, false, true, b_est);
+    base += kStep;
+    if (base >= p1) break;
+    load(vb, base + kStep);
+    step(va, base, false, true, b_est);
+    base += kStep;
   }
   if (lane == 0) s_cnt[wave] = cnt;
   __syncthreads();
+  uint32_t listed = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesTk; ++w) listed += s_cnt[w];
+  for (int i = tid; i < kBins1; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  if (listed >= (uint32_t)k) {
+    // at least k keys lie in buckets >= b_est, so the k-th largest does too,
+    // and the lists' histogram of those buckets is the row's: b1 and the count
+    // above it follow from the listed keys alone
+    for (uint32_t e = lane; e < cnt; e += 64) {
+      uint32_t key;
+      if (e < (uint32_t)kRowCap) {
+        key = s_key[wave][e];
+      } else {
+        key = score_key(srow[my_spill[e]]);
+      }
+      atomicAdd(&hist[key >> 20], 1u);
+    }
+  } else {
+    // the sample over-estimated the threshold: histogram of the whole row,
+    // then (below) a compaction with the exact bucket
+    load(va, p0);
+    for (int base = p0;;) {
+      load(vb, base + kStep);
+      step(va, base, true, false, 0u);
+      base += kStep;
+      if (base >= p1) break;
+      load(va, base + kStep);
+      step(vb, base, true, false, 0u);
+      base += kStep;
+      if (base >= p1) break;
+    }
+  }
+  __syncthreads();
+  select_bucket<kBins1>(hist, (uint32_t)k, s_scan, s_out);
+  const uint32_t b1 = s_out[0];
+  const uint32_t n_above = s_out[1];
+  if (listed < (uint32_t)k) {
+    cnt = 0;
+    load(va, p0);
+    for (int base = p0;;) {
+      load(vb, base + kStep);
+      step(va, base, false, true, b1);
+      base += kStep;
+      if (base >= p1) break;
+      load(va, base + kStep);
+      step(vb, base, false, true, b1);
+      base += kStep;
+      if (base >= p1) break;
+    }
+    if (lane == 0) s_cnt[wave] = cnt;
+    __syncthreads();
+  }
 
-  // entry e of wave w's list and its key (keys of spilled candidates re-read)
+  // entry e of wave w's list: its position, and its key (re-read for spills)
   auto get = [&](int w, uint32_t e, uint32_t& key) -> uint32_t {
     if (e < (uint32_t)kRowCap) {
       key = s_key[w][e];
-      return s_ent[w][e];
+      return (uint32_t)(w * seg) + s_off[w][e];
     }
-    const uint32_t v = spill[(size_t)row * spill_stride + (size_t)w * seg_cap + e];
-    key = (v & kSure) ? 0u : score_key(srow[v & ~kSure]);
-    return v;
+    const uint32_t p = spill[(size_t)row * spill_stride + (size_t)w * seg_cap + e];
+    key = score_key(srow[p]);
+    return p;
   };
-  const uint32_t my_n = s_cnt[wave];
+  const uint32_t my_n = cnt;
 
-  // ---- digit 2 (bits 19..8), then digit 3 (bits 7..0), over the candidates ----
+  // ---- digit 2 (bits 19..8), then digit 3 (bits 7..0), over bucket b1 ----
   const uint32_t need1 = (uint32_t)k - n_above;
   for (int i = tid; i < kBins2; i += kThreads) hist[i] = 0;
   __syncthreads();
   for (uint32_t e = lane; e < my_n; e += 64) {
     uint32_t key;
-    const uint32_t v = get(wave, e, key);
-    if (!(v & kSure)) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
+    get(wave, e, key);
+    if ((key >> 20) == b1) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
   }
   __syncthreads();
   select_bucket<kBins2>(hist, need1, s_scan, s_out);
@@ -678,7 +737,7 @@ __global__ void __launch_bounds__(kThreads) topk_row_kernel(
   const uint32_t pre12 = (b1 << 12) | b2;
   uint32_t tau, need_tie;  // the smallest kept key; how many keys equal to it are kept
   if (s_out[2] == need2) {
-    // every candidate of bucket b2 is kept: no third digit
+    // every key of bucket b2 is kept: no third digit
     tau = pre12 << 8;
     need_tie = 0xFFFFFFFFu;
   } else {
@@ -687,8 +746,8 @@ __global__ void __launch_bounds__(kThreads) topk_row_kernel(
     __syncthreads();
     for (uint32_t e = lane; e < my_n; e += 64) {
       uint32_t key;
-      const uint32_t v = get(wave, e, key);
-      if (!(v & kSure) && (key >> 8) == pre12) atomicAdd(&hist[key & 0xFFu], 1u);
+      get(wave, e, key);
+      if ((key >> 8) == pre12) atomicAdd(&hist[key & 0xFFu], 1u);
     }
     __syncthreads();
     select_bucket<kBins3>(hist, need2, s_scan, s_out);
@@ -697,13 +756,14 @@ __global__ void __launch_bounds__(kThreads) topk_row_kernel(
   }
 
   // ---- emission in position order (wave order, then list order) ----
-  // ties per wave, then each wave's kept count, then the writes
+  // kept: every key above tau, and the first need_tie keys equal to tau
+  // (entries below bucket b1 are above no kept key and are passed over)
   uint32_t my_ties = 0;
   for (uint32_t e0 = 0; e0 < my_n; e0 += 64) {
     const uint32_t e = e0 + lane;
-    uint32_t key = 0, v = kSure;
-    if (e < my_n) v = get(wave, e, key);
-    my_ties += (uint32_t)__popcll(__ballot(e < my_n && !(v & kSure) && key == tau));
+    uint32_t key = 0;
+    if (e < my_n) get(wave, e, key);
+    my_ties += (uint32_t)__popcll(__ballot(e < my_n && key == tau));
   }
   if (lane == 0) s_tie[wave] = my_ties;
   __syncthreads();
@@ -713,18 +773,17 @@ __global__ void __launch_bounds__(kThreads) topk_row_kernel(
     uint32_t tie_rank = ties_before, kept = 0;
     for (uint32_t e0 = 0; e0 < my_n; e0 += 64) {
       const uint32_t e = e0 + lane;
-      uint32_t key = 0, v = 0;
-      bool in = e < my_n;
-      if (in) v = get(wave, e, key);
-      const bool sure = in && (v & kSure);
-      const bool tie = in && !sure && key == tau;
+      uint32_t key = 0, p = 0;
+      const bool in = e < my_n;
+      if (in) p = get(wave, e, key);
+      const bool tie = in && key == tau;
       const uint64_t tm = __ballot(tie);
       const uint32_t my_rank = tie_rank + (uint32_t)__popcll(tm & lt);
-      const bool sel = sure || (in && !sure && key > tau) || (tie && my_rank < need_tie);
+      const bool sel = (in && key > tau) || (tie && my_rank < need_tie);
       const uint64_t sm = __ballot(sel);
       if (write && sel) {
         const uint32_t at = out_base + kept + (uint32_t)__popcll(sm & lt);
-        if (at < (uint32_t)k) out[at] = (int32_t)(v & ~kSure);
+        if (at < (uint32_t)k) out[at] = (int32_t)p;
       }
       tie_rank += (uint32_t)__popcll(tm);
       kept += (uint32_t)__popcll(sm);

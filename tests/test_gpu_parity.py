@@ -286,6 +286,35 @@ def test_topk_row_kernel_spills(name):
     assert bad.size == 0, "rows differ: %s" % bad[:5].tolist()
 
 
+def test_topk_row_kernel_sample_miss():
+    """The row kernel estimates its threshold bucket from each wave's first
+    1024 positions (wave w covers [w seg, (w+1) seg), seg = ceil(L / 8)). Here
+    those windows hold 600 scores of 9, more than the sample rank it takes, so
+    the estimate lands on the bucket of 9, while the true threshold lies among
+    2000 tied scores of 8 placed outside the windows: the second compaction
+    pass must run and keep the 1448 lowest-positioned 8s. 512 identical rows,
+    against the oracle."""
+    _say("case: topk row kernel sample miss")
+    B, T, L, k = 1, 512, 100000, 2048
+    rs = np.random.default_rng(11)
+    row = rs.random(L).astype(np.float32)  # [0, 1): below both planted values
+    seg = -(-L // 8)
+    windows = np.concatenate([np.arange(w * seg, w * seg + 1024) for w in range(8)])
+    outside = np.setdiff1d(np.arange(L), windows)
+    row[rs.choice(windows, 600, replace=False)] = 9.0
+    row[rs.choice(outside, 2000, replace=False)] = 8.0
+    ref = oracle.topk(row[None, None, :], np.array([[L]], np.int32), k)[0, 0]
+    assert (row[ref] == 9.0).sum() == 600 and (row[ref] == 8.0).sum() == k - 600
+    ds = torch.from_numpy(row).to(DEV).view(1, 1, L).expand(B, T, L).contiguous()
+    dv = torch.full((B, T), L, dtype=torch.int32, device=DEV)
+    idx = torch.full((B, T, k), -7, dtype=torch.int32, device=DEV)
+    ws = _zeros(lcs.topk_workspace_bytes(B, T, L, k))
+    lcs.topk_select(ds, dv, k, idx, ws)
+    got = idx.cpu().numpy()[0]
+    bad = np.argwhere(np.any(got != ref[None, :], axis=-1))
+    assert bad.size == 0, "rows differ: %s" % bad[:5].tolist()
+
+
 def test_topk_workspace_reused_across_shapes():
     _say("case: topk workspace reuse")
     shapes = [(1, 1, 1 << 20, 2048), (4, 8, 30000, 2048), (1, 3, 7000, 512)]
