@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 METRIC = ("decode tokens/s/GPU at L=128K & 1M (indexer+top-k+sparse attn); % HBM roofline")
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 IDX_BYTES_PER_KEY = 132  # 128 E4M3 codes + fp32 scale
 IDX_PREFILL_MIN_T = 16  # T at which idx_score switches to the dense FP8-MFMA kernel
 IDX_BYTES_PER_QUERY = 32 * 128 + 32 * 4 + 32 * 4  # q8, q_scale, w
@@ -426,6 +427,40 @@ def step_bytes(w, off):
     return idx + att
 
 
+def _roof(amount, us, peak, unit, what):
+    achieved = amount / (us * 1e-6) / (1e9 if unit == "GB/s" else 1e12)
+    key = "bytes_per_launch" if unit == "GB/s" else "flop_per_launch"
+    return {"bound": "hbm" if unit == "GB/s" else "mfma", "achieved": round(achieved, 1),
+            "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), key: amount,
+            "avg_launch_us": round(us, 2), "counts": what}
+
+
+def kernel_rooflines(w, ker):
+    """The selection and the attention calls against their own bounds, from the
+    mean launch times in kernels_us (back-to-back launches between HIP events).
+    The selection reads every visible score once and writes k indices per
+    query; the attention (with its split combine, which the call launches)
+    reads the selected rows, its queries and selections and writes out and lse
+    (HBM), or, at many queries per sequence, performs 64 heads x (576 + 512)
+    MACs per selected row (bf16 MFMA)."""
+    q = w.B * w.T
+    vis = w.vis_len().astype("int64")
+    scores = int(vis.sum()) * 4 + q * w.k * 4
+    res = {"topk_select": _roof(scores, ker["topk_select"], HBM_PEAK_GBS, "GB/s",
+                                "visible scores read once + indices written")}
+    rows = int(vis.clip(max=w.k).sum())
+    if w.T >= IDX_PREFILL_MIN_T:
+        flops = 2.0 * rows * 64 * (576 + 512)
+        res["sparse_mla_attn"] = _roof(flops, ker["sparse_mla_attn"], BF16_PEAK_TFLOPS, "TFLOP/s",
+                                       "QK (576 dims) and PV (512 dims) per head and row")
+    else:
+        row = 580 if w.kv_fp8 else 1152
+        nbytes = rows * (row + 4) + q * ATT_BYTES_PER_QUERY_IO
+        res["sparse_mla_attn"] = _roof(nbytes, ker["sparse_mla_attn"], HBM_PEAK_GBS, "GB/s",
+                                       "selected rows + indices, q, out, lse")
+    return res
+
+
 def _unit(w):
     return ("draft tokens/s" if w.mtp_steps else
             "prefill tokens/s" if w.T >= IDX_PREFILL_MIN_T else
@@ -491,6 +526,7 @@ def measure(w, args, lcs, headline):
                 rec["roofline"]["copy_peak_measured"] = round(cp, 1)
                 rec["roofline"]["frac_of_copy_peak"] = round(achieved / cp, 4)
         rec["kernels_us"] = {k: round(v, 2) for k, v in ker.items()}
+        rec["kernel_rooflines"] = kernel_rooflines(w, ker)
         if headline and not args.no_extras:
             ap_us, ap_bytes = time_cache_append(w, lcs, 50)
             rec["cache_append"] = {"tokens": w.B * w.T, "us_per_launch": round(ap_us, 2),
