@@ -52,9 +52,18 @@ struct RowState {
 };
 
 // Many rows of moderate length take one workgroup per row (topk_row_kernel);
-// the others the chunked launches.
+// the others the chunked launches. Two row workgroups share a CU, so up to 512
+// rows run at once and the row kernel's time hardly depends on their number
+// (about 19 us + 0.24 ns per position of a row), while the chunked launches'
+// grows with rows x L (about 26 us + 2.1 ps per score): measured, the row
+// kernel wins from about 100 rows of 2^17 positions (192 rows: 57 against
+// 78 us) and loses below (32 rows: 54 against 35 us, and the decode composite
+// also builds the chunked launches' histogram inside the indexer).
 constexpr int kRowMaxL = 1 << 18;
-constexpr int kRowMinRows = 512;
+#ifndef LCS_TOPK_ROW_MIN_ROWS
+#define LCS_TOPK_ROW_MIN_ROWS 128
+#endif
+constexpr int kRowMinRows = LCS_TOPK_ROW_MIN_ROWS;
 __host__ __device__ inline bool uses_row_kernel(int64_t rows, int L) {
   return L <= kRowMaxL && rows >= kRowMinRows;
 }

@@ -236,7 +236,7 @@ TOPK_CASES = [
     # more entries around the threshold than the final kernel holds in
     # registers (16384): its passes over the lists in global memory
     ("equal", 1, 2, 40000, 2048),
-    # >= 512 rows of <= 2^18 positions: the one-workgroup-per-row kernel
+    # >= 128 rows of <= 2^18 positions: the one-workgroup-per-row kernel
     ("normal", 1, 600, 4001, 2048), ("ragged", 1, 520, 20000, 2048),
     ("signed-zero", 2, 256, 3000, 1000), ("ties", 4, 128, 9000, 2048),
 ]
@@ -554,7 +554,7 @@ FUSED_CASES = [
     # one chunk per row (L <= 2048) with rows longer than k
     ("one-chunk", 3, 2000, 1000, 2, wl.SCHED_GROUP4,
      ([[2000], [1001], [999]], [[1000], [0], [2000]])),
-    # >= 512 rows of <= 2^18 positions: the one-workgroup-per-row top-k, so
+    # >= 128 rows of <= 2^18 positions: the one-workgroup-per-row top-k, so
     # the composite keeps the indexer and the selection separate
     ("row-kernel", 520, 3000, 2048, 2, wl.SCHED_GROUP4,
      ([[3000]] * 519 + [[100]], [[2049]] * 520)),
