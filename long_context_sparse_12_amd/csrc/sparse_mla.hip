@@ -1179,47 +1179,57 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
 // the attention kernels' own log2 partials, log2(e) for natural-log lse).
 // Partial s of query q sits at part_o + q * o_q + s * o_s (elements) and
 // part_lse + q * l_q + s * l_s: query-major for the splits of one launch,
-// shard-major for outputs gathered from several devices. 256 threads per workgroup = G split groups x 256/G columns
-// of four output elements; a workgroup covers 1024/G consecutive elements of
-// a query's [64 heads][512] output, so a query spreads over 32 G workgroups.
-// Group g folds splits g, g + G, g + 2G, ... with a running maximum, the
-// loads of up to eight of its splits in flight at a time; with G > 1 the
-// groups' partial states then merge through LDS. G = 1 serves up to eight
-// splits in one memory latency per thread, G = 4 up to 32.
+// shard-major for outputs gathered from several devices. 256 threads per
+// workgroup = G split groups x 256/G columns of E output elements (E = 4 or
+// 8: one 8- or 16-byte load per split); a workgroup covers 256 E / G
+// consecutive elements of a query's [64 heads][512] output, so a query
+// spreads over 128 G / E workgroups. Group g folds splits g, g + G, g + 2G,
+// ... with a running maximum, the loads of up to eight of its splits in
+// flight at a time; with G > 1 the groups' partial states then merge through
+// LDS. G = 1 serves up to eight splits in one memory latency per thread,
+// G = 4 up to 32.
 constexpr int kCombBatch = 8;
-template <int G>
+template <int E>
+struct BfVec;
+template <>
+struct BfVec<4> { using T = v2i; };
+template <>
+struct BfVec<8> { using T = v4i; };
+
+template <int G, int E>
 __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
                                                       int splits, int64_t o_q, int64_t o_s,
                                                       int64_t l_q, int64_t l_s, float l_mul,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
+  using Vec = typename BfVec<E>::T;
   constexpr int kCols = 256 / G;
-  __shared__ v4f s_acc[G > 1 ? G - 1 : 1][kCols];
+  constexpr int kWords = E / 2;  // bf16 pairs per thread
+  __shared__ float s_acc[G > 1 ? G - 1 : 1][E][kCols];
   __shared__ float s_m[G], s_w[G];
   const int qi = blockIdx.y;
   const int tid = threadIdx.x, grp = tid / kCols, col = tid % kCols;
   const int64_t per_split = (int64_t)kAttHeads * kLatent;
-  const int e = blockIdx.x * (4 * kCols) + 4 * col;  // element within a split's output
+  const int e = blockIdx.x * (E * kCols) + E * col;  // element within a split's output
   const int head = e / kLatent;
   const uint16_t* base = part_o + (int64_t)qi * o_q + e;
   const float* lbase = part_lse + (int64_t)qi * l_q + head;
   float m = -INFINITY, wsum = 0.f;
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) acc[i] = 0.f;
   for (int s0 = grp; s0 < splits; s0 += G * kCombBatch) {
     const int nb = min(kCombBatch, (splits - s0 + G - 1) / G);  // this group's splits in the batch
     float l[kCombBatch];
-    v4f o[kCombBatch];
+    Vec x[kCombBatch];
 #pragma unroll
     for (int j = 0; j < kCombBatch; ++j) {
       l[j] = -INFINITY;
-      o[j] = v4f{0.f, 0.f, 0.f, 0.f};
       if (j < nb) {
         const int64_t sp = s0 + G * j;
         l[j] = lbase[sp * l_s] * l_mul;
-        const v2i x = *(const v2i*)(base + sp * o_s);  // four bf16
-        o[j] = v4f{__uint_as_float((uint32_t)x[0] << 16), __uint_as_float((uint32_t)x[0] & 0xFFFF0000u),
-                   __uint_as_float((uint32_t)x[1] << 16), __uint_as_float((uint32_t)x[1] & 0xFFFF0000u)};
+        x[j] = *(const Vec*)(base + sp * o_s);  // E bf16
       }
     }
     float m_new = m;
@@ -1227,22 +1237,34 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
     for (int j = 0; j < kCombBatch; ++j) m_new = fmaxf(m_new, l[j]);
     if (m_new == -INFINITY) continue;  // no valid row in these splits yet
     const float sc = m == -INFINITY ? 0.f : exp2f(m - m_new);
-    acc *= sc;
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] *= sc;
     wsum *= sc;
 #pragma unroll
     for (int j = 0; j < kCombBatch; ++j) {
+      if (j >= nb) continue;
       const float w = l[j] == -INFINITY ? 0.f : exp2f(l[j] - m_new);
-      acc += o[j] * w;
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) {
+        const uint32_t u = (uint32_t)x[j][i];
+        acc[2 * i] += __uint_as_float(u << 16) * w;
+        acc[2 * i + 1] += __uint_as_float(u & 0xFFFF0000u) * w;
+      }
       wsum += w;
     }
     m = m_new;
   }
   float mx = m, wt = wsum;
-  v4f o = acc;
+  float o[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) o[i] = acc[i];
   if (G > 1) {
     // the threads of a group that serve one head hold the same m and wsum
-    // (they depend on that head's lse values only); a workgroup spans one head
-    if (grp > 0) s_acc[grp - 1][col] = acc;
+    // (they depend on that head's lse values only); a workgroup spans whole heads
+    if (grp > 0) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) s_acc[grp > 0 ? grp - 1 : 0][i][col] = acc[i];
+    }
     if (col == 0) {
       s_m[grp] = m;
       s_w[grp] = wsum;
@@ -1252,20 +1274,24 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t* __restrict
     mx = s_m[0];
 #pragma unroll
     for (int g = 1; g < G; ++g) mx = fmaxf(mx, s_m[g]);
-    wt = 0.f;
-    o = v4f{0.f, 0.f, 0.f, 0.f};
+    const float f0 = s_m[0] == -INFINITY ? 0.f : exp2f(s_m[0] - mx);
+    wt = s_w[0] * f0;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int i = 0; i < E; ++i) o[i] = acc[i] * f0;
+#pragma unroll
+    for (int g = 1; g < G; ++g) {
       const float mg = s_m[g];
       const float f = mg == -INFINITY ? 0.f : exp2f(mg - mx);
       wt += s_w[g] * f;
-      o += (g == 0 ? acc : s_acc[g > 0 ? g - 1 : 0][col]) * f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) o[i] += s_acc[g - 1][i][col] * f;
     }
   }
   const float inv = wt > 0.f ? 1.f / wt : 0.f;
-  o *= inv;
-  *(v2i*)(out + (int64_t)qi * per_split + e) =
-      v2i{(int)pack_bf16x2(o[0], o[1]), (int)pack_bf16x2(o[2], o[3])};
+  Vec y;
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) y[i] = (int)pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
+  *(Vec*)(out + (int64_t)qi * per_split + e) = y;
   if (lse && (e & (kLatent - 1)) == 0)
     lse[(int64_t)qi * kAttHeads + head] = wt > 0.f ? (mx + log2f(wt)) * kLn2 : -INFINITY;
 }
@@ -1379,15 +1405,21 @@ hipError_t launch_sparse_mla_paged(const uint16_t* q, const void* kv, bool kv_fp
   return launch_split_combine(part_o, part_lse, p.splits, queries, out, lse, stream);
 }
 
+// output elements per combine thread: 16-byte loads where one group folds
+// every split (32 queries x 8 splits: 4.9 against 5.5 us per launch; 192 x 8:
+// 22.0 against 25.9), 8-byte loads for the four-group kernel, whose few
+// queries need the workgroups (2 x 16 splits: 4.5 against 4.4 us)
+constexpr int kCombE1 = 8, kCombE4 = 4;
+
 hipError_t launch_split_combine(const uint16_t* part_o, const float* part_lse, int splits,
                                 int64_t queries, uint16_t* out, float* lse, hipStream_t stream) {
   const SplitPlan p{splits, 0};
   const int64_t per = (int64_t)kAttHeads * kLatent;
   if (p.splits <= kCombBatch)
-    return launch_kernel(combine_kernel<1>, dim3(32, (unsigned)queries), dim3(256), 0, stream,
+    return launch_kernel(combine_kernel<1, kCombE1>, dim3(128 / kCombE1, (unsigned)queries), dim3(256), 0, stream,
                          part_o, part_lse, p.splits, p.splits * per, per,
                          (int64_t)p.splits * kAttHeads, (int64_t)kAttHeads, 1.0f, out, lse);
-  return launch_kernel(combine_kernel<4>, dim3(32 * 4, (unsigned)queries), dim3(256), 0, stream,
+  return launch_kernel(combine_kernel<4, kCombE4>, dim3(128 * 4 / kCombE4, (unsigned)queries), dim3(256), 0, stream,
                        part_o, part_lse, p.splits, p.splits * per, per,
                        (int64_t)p.splits * kAttHeads, (int64_t)kAttHeads, 1.0f, out, lse);
 }
@@ -1398,10 +1430,10 @@ hipError_t launch_lse_combine(const uint16_t* part_out, const float* part_lse, i
   const int64_t per = (int64_t)kAttHeads * kLatent;
   if (queries == 0) return hipSuccess;
   if (G <= kCombBatch)
-    return launch_kernel(combine_kernel<1>, dim3(32, (unsigned)queries), dim3(256), 0, stream,
+    return launch_kernel(combine_kernel<1, kCombE1>, dim3(128 / kCombE1, (unsigned)queries), dim3(256), 0, stream,
                          part_out, part_lse, G, per, queries * per, (int64_t)kAttHeads,
                          queries * kAttHeads, kLog2e, out, lse);
-  return launch_kernel(combine_kernel<4>, dim3(32 * 4, (unsigned)queries), dim3(256), 0, stream,
+  return launch_kernel(combine_kernel<4, kCombE4>, dim3(128 * 4 / kCombE4, (unsigned)queries), dim3(256), 0, stream,
                        part_out, part_lse, G, per, queries * per, (int64_t)kAttHeads,
                        queries * kAttHeads, kLog2e, out, lse);
 }
