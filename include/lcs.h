@@ -194,7 +194,10 @@ size_t lcs_indexshare_workspace_bytes(int32_t B, int32_t T, int32_t L, int32_t k
  * latest full layer's selection. mtp_steps > 0 (MTP draft reuse): layers[]
  * holds mtp_steps draft steps of one layer; step 0 runs the indexer, and
  * every step attends with step 0's selection over step 0's kv/kv_scale (KV
- * Share), each with its own q, out and lse. */
+ * Share), each with its own q, out and lse. With LCS_ROCTX=1 in the
+ * environment each layer's launches sit in a roctx range ("lcs layer 6
+ * shared", "lcs layer 2 full") for rocprofv3 --marker-trace; the roctx
+ * library is loaded at run time, and is not needed otherwise. */
 lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers,
                                   lcs_sched sched, const uint8_t* full_mask,
                                   int32_t mtp_steps, lcs_kv_dtype kv_dtype,

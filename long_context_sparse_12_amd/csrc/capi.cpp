@@ -3,11 +3,14 @@
 //
 // Validation runs before any HIP call, so every error path can be exercised
 // without a GPU.
+#include <dlfcn.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/lcs.h"
@@ -322,6 +325,54 @@ int enum_bits(const E& e) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Per-layer ranges for profilers (rocprofv3 --marker-trace): with LCS_ROCTX=1
+// in the environment, lcs_indexshare_forward brackets each layer's launches
+// with a roctx range ("lcs layer 6 shared", "lcs layer 2 full"). The two roctx
+// entry points are looked up in ROCm's roctx library at the first call, so
+// liblcs has no link-time dependency on it; without the variable, or without
+// the library, nothing is called.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const Roctx& roctx() {
+  static Roctx r;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const char* e = getenv("LCS_ROCTX");
+    if (!e || strcmp(e, "1") != 0) return;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (!h) return;
+    auto push = (int (*)(const char*))dlsym(h, "roctxRangePushA");
+    auto pop = (int (*)())dlsym(h, "roctxRangePop");
+    if (push && pop) {
+      r.push = push;
+      r.pop = pop;
+    }
+  });
+  return r;
+}
+
+// one layer's range, closed on every way out of the layer's launches
+class LayerRange {
+ public:
+  LayerRange(int32_t layer, bool full) : r_(roctx()) {
+    if (!r_.push) return;
+    char msg[48];
+    snprintf(msg, sizeof(msg), "lcs layer %d %s", (int)layer, full ? "full" : "shared");
+    r_.push(msg);
+  }
+  ~LayerRange() {
+    if (r_.pop) r_.pop();
+  }
+  LayerRange(const LayerRange&) = delete;
+  LayerRange& operator=(const LayerRange&) = delete;
+
+ private:
+  const Roctx& r_;
+};
 
 }  // namespace
 
@@ -738,6 +789,7 @@ lcs_status lcs_indexshare_forward(const lcs_layer* layers, int32_t n_layers, lcs
   for (int32_t l = 0; l < n_layers; ++l) {
     const lcs_layer& ly = layers[l];
     const bool full = mtp_steps > 0 ? l == 0 : is_full_layer(sched, l, full_mask);
+    const LayerRange range(l, full);
     if (full) {
       cur = idx_out + (size_t)nfull * per;
       ++nfull;
