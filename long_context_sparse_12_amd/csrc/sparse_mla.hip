@@ -504,9 +504,13 @@ __device__ __forceinline__ Role role_of(int wave) {
 #define LCS_ATTN_B_MAX_SPLITS 16  // fewer, longer splits pipeline better than a wider combine
 #endif
 
+// Splits per query: as many as fit one round of workgroups (one per CU), so
+// no launch ends with a partial second round: 192 verify queries take one
+// split each (192 workgroups, no combine) rather than two (384 workgroups,
+// the second round on half the CUs, and a combine).
 __host__ __device__ inline SplitPlan plan_splits_b(int64_t queries, int k) {
   SplitPlan p;
-  int64_t s = (LCS_ATTN_B_TARGET_WGS + queries - 1) / queries;
+  int64_t s = LCS_ATTN_B_TARGET_WGS / queries;
   const int64_t max_s = (k + kTileRows - 1) / kTileRows;
   if (s > max_s) s = max_s;
   if (s > LCS_ATTN_B_MAX_SPLITS) s = LCS_ATTN_B_MAX_SPLITS;
