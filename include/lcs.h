@@ -122,6 +122,10 @@ size_t lcs_attn_workspace_bytes(int32_t B, int32_t T, int32_t k);
  * out [B][T][64][512] bf16 = softmax_i(sm_scale * q . kv[idx_i]) . kv[idx_i][0:512]
  * lse [B][T][64] fp32 natural-log sum of exp of the scaled logits (nullable);
  * a query with no valid index gets out = 0 and lse = -inf.
+ * The kernels gather the sequence's position 0 for each -1 slot and weight it
+ * zero: position 0 of a sequence with any valid index must hold finite
+ * values (the first token's row always does); a query with no valid index
+ * outputs zeros whatever that row holds.
  * Positions outside [-1, L) are a caller error (not checked on the device). */
 lcs_status lcs_sparse_mla_attn(const uint16_t* q, const void* kv,
                                lcs_kv_dtype kv_dtype, const float* kv_scale,
@@ -328,7 +332,9 @@ lcs_status lcs_idx_score_paged(const uint8_t* q8, const float* q_scale, const fl
                                int32_t T, int32_t L, float* scores, hipStream_t stream);
 
 /* lcs_sparse_mla_attn over a paged latent cache; workspace as
- * lcs_attn_workspace_bytes(B, T, k). Pools may exceed 4 GB. */
+ * lcs_attn_workspace_bytes(B, T, k). Pools may exceed 4 GB. -1 slots gather
+ * position 0 through the sequence's first table entry, never an unmapped
+ * block. */
 lcs_status lcs_sparse_mla_attn_paged(const uint16_t* q, const void* kv_pool,
                                      lcs_kv_dtype kv_dtype, const float* kv_scale_pool,
                                      const lcs_paged* paged, const int32_t* idx, int32_t B,

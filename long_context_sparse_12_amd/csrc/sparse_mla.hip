@@ -167,7 +167,8 @@ __device__ __forceinline__ void issue_tile(AttnCtx<FP8>& c, int tile) {
   for (int i = 0; i < C::kPerHi; ++i) {
     const int j = c.wave + kWavesA * i;
     if (j < C::kInstr) {
-      const int32_t s = rows[i] >= 0 ? rows[i] : 0;  // padding rows load row 0 (masked below)
+      // padding rows load the sequence's first row (weighted zero below)
+      const int32_t s = rows[i] >= 0 ? rows[i] : 0;
       dma16(c.kv8 + (c.kv_b + s) * (int64_t)(FP8 ? kKvDim : kRowBytes) + 16 * gran[i],
             dst + j * 1024);
     }
@@ -442,6 +443,15 @@ __global__ void __launch_bounds__(kThreadsA) sparse_mla_kernel(
   uint8_t* ebuf = eslot == 0 ? c.st[0] : eslot == 1 ? c.st[1] : eslot == 2 ? c.st[2] : c.cvt;
   uint8_t* eb = ebuf + (FP8 ? (c.wave & 1) : (c.wave & 3)) * kEpiWave;
   const int ln = c.lane & 31;
+  // a head with no visible row writes zeros, whatever its padding rows held
+  // (0 x NaN is not 0). All heads of a query share its rows, so this is rare
+  // and, for finite logits, the same for the whole wave: a scalar branch.
+  if (!__all(l_tot > 0.f)) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c.acc[mt][i] = l_tot > 0.f ? c.acc[mt][i] : 0.f;
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -552,6 +562,7 @@ struct AttnB {
   int lbs, nblk;         // paged: log2 rows per block, blocks in the pool
   int n_rows, n_tiles;
   int wave, lane, hg;
+  uint32_t pad_row;  // the row padding entries load: the sequence's position 0 (paged: its pool row)
 };
 
 // A split may hold all k selected rows, so its positions do not sit in LDS
@@ -594,7 +605,7 @@ __device__ __forceinline__ int32_t pool_row(const AttnB& c, int32_t p, int32_t b
 // need the positions): tile t's scales go into slot t & 3 of the scale ring
 // in step t-3 and are read by the S waves in step t-1.
 __device__ __forceinline__ float load_scale(const AttnB& c, int32_t p) {
-  return c.kscale[p >= 0 ? p : 0];
+  return c.kscale[p >= 0 ? p : 0];  // padding rows: replaced by 1 in s_phase
 }
 __device__ __forceinline__ void scale_put(const AttnB& c, int tile, float v) {
   if (c.lane < kTileRows) c.sring[(tile & (kPosSlots - 1)) * kTileRows + c.lane] = v;
@@ -649,7 +660,9 @@ __device__ __forceinline__ void fetch_fp8(const AttnB& c, GWave8& w, int tile) {
   for (int i = 0; i < kFp8Per; ++i) rows[i] = slot[w.row[i]];
 #pragma unroll
   for (int i = 0; i < kFp8Per; ++i) {
-    const uint32_t s = rows[i] >= 0 ? (uint32_t)rows[i] : 0u;  // padding rows load row 0 (masked)
+    // padding rows load the sequence's first row (position 0; paged: its first
+    // table entry's pool row), weighted zero
+    const uint32_t s = rows[i] >= 0 ? (uint32_t)rows[i] : c.pad_row;
     if (PAGED)  // pool row: a 64-bit offset (pools may exceed 4 GB)
       w.fr[B][i] = *(const v4i*)(w.kvb + ((uint64_t)s * kKvDim + (uint32_t)w.src[i]));
     else  // 32-bit offset from the sequence base (the launcher keeps L * 576 < 2^32)
@@ -688,7 +701,9 @@ __device__ __forceinline__ void issue_tile_b(const AttnB& c, const GWave& w, int
   for (int i = 0; i < kDmaPerB; ++i) rows[i] = pos_slot(c, tile)[w.dma_row[i]];
 #pragma unroll
   for (int i = 0; i < kDmaPerB; ++i) {
-    const uint32_t s = rows[i] >= 0 ? (uint32_t)rows[i] : 0u;  // padding rows load row 0 (masked)
+    // padding rows load the sequence's first row (position 0; paged: its first
+    // table entry's pool row), weighted zero
+    const uint32_t s = rows[i] >= 0 ? (uint32_t)rows[i] : c.pad_row;
     if (PAGED)  // pool row: a 64-bit offset (pools may exceed 4 GB)
       dma16(w.kvb + ((uint64_t)s * kRowBytes + (uint32_t)w.dma_off[i]),
             c.st[S] + 1024 * (w.g + kGatherWaves * i));
@@ -757,10 +772,15 @@ __device__ __forceinline__ void s_phase(const AttnB& c, SWave& w, int tile, int 
   for (int i = 0; i < 16; ++i) t[i] = FP8 ? (se[i] + so[i]) * psc[i] : se[i] + so[i];
   const bool all_valid = valid == 0xFFFFFFFFu;
   if (!all_valid) {
+    // padding rows: no logit, and scale 1 (their P entry is 0, and the scale
+    // loaded for them, of row 0, need not be finite)
     const uint32_t mine = valid >> (4 * h);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (!((mine >> (8 * (i >> 2) + (i & 3))) & 1u)) t[i] = -INFINITY;
+      if (!((mine >> (8 * (i >> 2) + (i & 3))) & 1u)) {
+        t[i] = -INFINITY;
+        if (FP8) psc[i] = 1.f;
+      }
   }
   float mx = t[0];
 #pragma unroll
@@ -970,6 +990,7 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   c.btab = PAGED ? block_table + (int64_t)b * max_blocks : nullptr;
   c.lbs = lbs;
   c.nblk = n_blocks;
+  c.pad_row = PAGED ? (uint32_t)min(max(c.btab[0], 0), n_blocks - 1) << lbs : 0u;
   c.lane = tid & 63;
   c.wave = tid >> 6;
   const Role role = role_of(c.wave);
@@ -1152,6 +1173,15 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
   constexpr int kEpiRow = 528;
   static_assert(32 * kEpiRow <= kTileBytes, "epilogue staging");
   uint8_t* eb = pw == 0 ? c.st[0] : pw == 1 ? c.st[1] : pw == 2 ? c.st[2] : c.st[3];  // not c.st[pw]: scratch
+  // a head with no visible row writes zeros, whatever its padding rows held
+  // (0 x NaN is not 0). All heads of a query share its rows, so this is rare
+  // and, for finite logits, the same for the whole wave: a scalar branch.
+  if (!__all(l_tot > 0.f)) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w.acc[mt][i] = l_tot > 0.f ? w.acc[mt][i] : 0.f;
+  }
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll

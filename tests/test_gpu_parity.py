@@ -418,6 +418,68 @@ def test_sparse_mla_empty_selection():
     assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_sparse_mla_padding_rows(fp8):
+    """Padding entries (-1) stand for no row: the kernels gather the
+    sequence's own position 0 for them (paged: through its first table entry)
+    and weight it zero, so a non-finite row 0 of an unmapped pool block does
+    not matter. A query with no selected row outputs exact zeros and lse = -inf
+    even where its sequence's position 0 is not finite. With and without
+    splits (3 and 300 queries); paged equal to contiguous bit for bit."""
+    from tests.test_gpu_paged import _pool
+    for B, T in ((3, 1), (100, 3)):
+        _say("case: sparse_mla padding rows, fp8=%d B=%d T=%d" % (fp8, B, T))
+        L, k = 3000, 256
+        q, kv, sc, idx = _attn_inputs(B, T, L, k, fp8, seed=17 + B, pad=40)
+        idx[idx == 0] = -1  # row 0 is never selected (padding may sit in any slot)
+        idx[0] = -1  # sequence 0: no selected row at all
+        assert not (idx == 0).any() and (idx[1:] < 0).any()
+        _, ref_lse, ref64 = oracle.sparse_mla(q, kv, sc, idx, 1 / 24, want64=True)
+        bad_kv = kv.copy()
+        bad_sc = None if sc is None else sc.copy()
+        # non-finite position 0 in the sequence with no selection
+        if fp8:
+            bad_kv[0, 0] = 0x7F  # E4M3 NaN
+            bad_sc[0, 0] = np.inf
+        else:
+            bad_kv[0, 0] = 0x7FC0  # bf16 NaN
+        kv_d, idx_d, q_d = to_dev(bad_kv), to_dev(idx), to_dev(q)
+        sc_d = None if sc is None else to_dev(bad_sc)
+        ws = _zeros(lcs.attn_workspace_bytes(B, T, k))
+        out = torch.empty((B, T, 64, 512), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((B, T, 64), dtype=torch.float32, device=DEV)
+        lcs.sparse_mla_attn(q_d, kv_d, sc_d, idx_d, 1 / 24, out, lse, ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all()
+        assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+        check_attention(out, ref64, lse, ref_lse.astype(np.float64))
+        # paged, with pool row 0 in a block no position maps to (the table uses
+        # blocks 1..), NaN there too
+        rs = np.random.default_rng(5 + B)
+        nb_seq = (L + 63) // 64
+        nb = B * nb_seq + 3
+        table = np.zeros((B, nb_seq + 1), np.int32)
+        table[:, :nb_seq] = 1 + rs.permutation(nb - 1)[:B * nb_seq].reshape(B, nb_seq)
+        pos = np.arange(L)
+        rows = torch.from_numpy(table[:, pos // 64].astype(np.int64) * 64 + pos % 64).to(DEV)
+        pg = lcs.Paged(to_dev(table), 64, nb)
+        kvp = _pool(kv_d, rows, nb, 64)
+        scp = None if sc is None else _pool(sc_d, rows, nb, 64)
+        flat = kvp.view((nb * 64,) + tuple(kvp.shape[2:]))
+        if fp8:
+            flat[0] = 0x7F
+            scp.view(-1)[0] = float("inf")
+        else:
+            flat.view(torch.int16)[0] = 0x7FC0
+        out_p = torch.empty_like(out)
+        lse_p = torch.empty_like(lse)
+        lcs.sparse_mla_attn_paged(q_d, kvp, scp, pg, idx_d, L, 1 / 24, out_p, lse_p, ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out_p.float()).all()
+        assert torch.equal(out_p.view(torch.int16), out.view(torch.int16))
+        assert torch.equal(lse_p.view(torch.int32), lse.view(torch.int32))
+
+
 @pytest.mark.parametrize("fp8", [True, False], ids=["fp8", "bf16"])
 def test_sparse_mla_rows_past_32bit_offsets(fp8):
     """A sequence whose KV rows reach past 2^32 bytes (4.3 GB of KV for one
