@@ -1058,6 +1058,12 @@ __global__ void __launch_bounds__(kThreadsB) sparse_mla_b_kernel(
       scale_put(c, 1, s1);
     }
     lds_barrier();  // prologue (tile 0 landed)
+    // The query has landed by now (tile 0's logits need all of it). Waiting
+    // for it here, before the steps, also tells the compiler so: otherwise it
+    // keeps the query loads pending through the step loop and waits with
+    // vmcnt(0) before the last logit MFMA of every step, which also waits for
+    // the position load S wave 0 issued in that step for the next one.
+    wait_vm<0>();
     s_step<3, FP8, PAGED>(c, w, -1);  // scores tile 0 from stage 0
     for (int j = 0; j < c.n_tiles; j += kStagesB) {
       s_step<0, FP8, PAGED>(c, w, j);
