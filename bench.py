@@ -52,9 +52,9 @@ CPU_WORKERS_MAX = 16  # oracle processes of the all-cores leg (the host's share 
 # scaled by the copy-kernel calibration; valid only for the kernel source it was
 # taken on (sha256 of csrc/idx_score.hip, first 16 hex digits).
 TRAFFIC = {
-    "decode-B32-L131072-group4": {"sha": "c879e1043bd19435", "bytes": 572725291},
-    "decode-B2-L1048576-78layers-fp8kv": {"sha": "c879e1043bd19435", "bytes": 285335363},
-    "mtp-B8-L1048576-7steps-fp8kv": {"sha": "c879e1043bd19435", "bytes": 1142141696},
+    "decode-B32-L131072-group4": {"sha": "c879e1043bd19435", "bytes": 572730834},
+    "decode-B2-L1048576-78layers-fp8kv": {"sha": "c879e1043bd19435", "bytes": 285335671},
+    "mtp-B8-L1048576-7steps-fp8kv": {"sha": "c879e1043bd19435", "bytes": 1142176075},
 }
 
 WORKLOAD_KEYS = ["tiny", "decode128k", "prefill", "decode1m", "mtp1m", "verify128k"]
